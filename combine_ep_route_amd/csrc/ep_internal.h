@@ -1,0 +1,191 @@
+// Internal declarations of libep: group/handle state and kernel launchers.
+// Not installed; the public interface is include/ep.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/ep.h"
+
+#define EP_API extern "C" __attribute__((visibility("default")))
+
+namespace ep {
+
+// Build limits (checked at group creation).
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kMaxNodes = 64;
+constexpr int kMaxRanks = 1024;
+constexpr int kMaxHidden = 16384;
+constexpr int kLayoutTile = 256;   // tokens per layout workgroup
+
+constexpr uint32_t kGroupMagic = 0x45504752u;   // "EPGR"
+constexpr uint32_t kHandleMagic = 0x4550484Eu;  // "EPHN"
+constexpr uint32_t kDeadMagic = 0xDEADDEADu;
+
+struct Handle;
+
+struct Group {
+  uint32_t magic = kGroupMagic;
+  ep_config_t cfg{};
+  int R = 0;          // ranks
+  int L = 0;          // experts per rank
+  int P = 0;          // experts per node
+  int J = 0;          // experts summed per node score (0 = no node limit)
+  int M = 0;          // nodes kept (0 = no limit)
+  int fp8 = 1;        // payload is FP8 (else BF16)
+  int64_t row_bytes = 0;   // FP8: H + H/128*4; BF16: 2H
+  int64_t msg_bytes = 0;   // LL: row_bytes + 16
+  int64_t n_max = 0;       // S * T_max
+  int64_t rows1_max = 0;   // HT stage-1 rows, worst case
+  int64_t rows2_max = 0;   // HT stage-2 rows, worst case (n_max * K)
+  int tiles_max = 0;       // layout tiles, worst case
+
+  // Device buffers (owned).
+  struct Alloc { void* ptr; size_t bytes; };
+  std::vector<Alloc> allocs;
+  int64_t bytes = 0;
+  uint8_t* ll_buf = nullptr;
+  uint8_t* st1 = nullptr;
+  int32_t* m1_tok = nullptr;
+  int32_t* m1_src = nullptr;
+  int32_t* m1_topk = nullptr;
+  float* m1_w = nullptr;
+  uint8_t* st2 = nullptr;
+  int32_t* m2_src = nullptr;
+  int32_t* m2_tok = nullptr;
+  int32_t* m2_k = nullptr;
+  int32_t* err = nullptr;
+
+  std::vector<Handle*> handles;
+
+  // Device facts, read at the first launch.
+  bool dev_ready = false;
+  int device = -1;
+  int num_cu = 0;
+};
+
+struct Handle {
+  uint32_t magic = kHandleMagic;
+  Group* g = nullptr;
+  bool in_use = false;
+  int64_t n = 0;   // tokens (S*T)
+  int T = 0;       // tokens per source
+  int tps = 0;     // layout tiles per source
+  int n_tiles = 0;
+  hipStream_t stream = nullptr;
+  int32_t* topk = nullptr;       // copy of topk_idx [n_max, K]
+  int32_t* slot_map = nullptr;   // LL [n_max, K]
+  int32_t* ll_count = nullptr;   // LL [E, S]
+  int32_t* node_row = nullptr;   // HT [n_max, N]
+  int32_t* row2 = nullptr;       // HT [n_max, K]
+  int32_t* c1 = nullptr;         // HT [R]
+  int32_t* off1 = nullptr;       // HT [R]
+  int32_t* c2 = nullptr;         // HT [E]
+  int32_t* off2 = nullptr;       // HT [E]
+  int32_t* hist_e = nullptr;     // [tiles_max, E]
+  int32_t* hist_n = nullptr;     // [tiles_max, N]
+};
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (one translation unit each).  All return hipSuccess or the
+// launch error; they enqueue on `stream` and never synchronise.
+// ---------------------------------------------------------------------------
+
+struct RouteArgs {
+  const float* scores;
+  int64_t ld;        // row stride of scores, elements
+  int64_t n;
+  int E, N, K, M, J;
+  int32_t* topk;     // [n, K]
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
+
+struct LayoutArgs {
+  const int32_t* topk;   // [n, K]
+  int64_t n;
+  int S, T, K, E, N, G, P;
+  int slots;             // LL slots per (expert, source)
+  int ht;                // 1 = HT maps, 0 = LL maps
+  int tps, n_tiles;
+  int32_t* hist_e;
+  int32_t* hist_n;
+  int32_t* topk_copy;    // [n, K]
+  int32_t* slot_map;
+  int32_t* ll_count;
+  int32_t* node_row;
+  int32_t* row2;
+  int32_t* c1;
+  int32_t* off1;
+  int32_t* c2;
+  int32_t* off2;
+  int32_t* err;
+};
+hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+// Set `count` int32 values to `value` with a small kernel (stream-ordered,
+// capture-safe).
+hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t stream);
+
+struct DispatchArgs {
+  const void* x;          // BF16 [n, H] or FP8 [n, H]
+  int64_t ld_x;           // elements
+  const float* x_scales;  // FP8 input only: [n, H/128]
+  int64_t ld_s;
+  int in_fp8;             // tokens arrive quantised
+  int out_fp8;            // payload is FP8
+  int64_t n;
+  int T, K, N, H;
+  int64_t row_bytes, msg_bytes;
+  int ht;
+  int max_blocks;         // 0 = one workgroup per token
+  // LL
+  const int32_t* slot_map;
+  uint8_t* ll_buf;
+  // HT
+  const int32_t* topk;
+  const float* w;
+  const int32_t* node_row;
+  const int32_t* row2;
+  uint8_t* st1;
+  int32_t* m1_tok;
+  int32_t* m1_src;
+  int32_t* m1_topk;
+  float* m1_w;
+  uint8_t* st2;
+  int32_t* m2_src;
+  int32_t* m2_tok;
+  int32_t* m2_k;
+};
+hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
+
+struct CombineArgs {
+  const uint16_t* y;      // BF16 rows
+  int64_t ld_y;           // elements
+  int64_t rows;           // rows available in y
+  const float* w;         // [n, K]
+  const int32_t* loc;     // [n, K]
+  int64_t n;
+  int K, H;
+  uint16_t* out;
+  int64_t ld_out;
+  int max_blocks;         // 0 = no cap
+  int32_t* err;
+};
+hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+struct DequantArgs {
+  const uint8_t* rows;
+  int64_t row_stride;     // bytes
+  int64_t n;
+  int H;
+  int fp8;
+  uint16_t* y;
+  int64_t ld_y;           // elements
+};
+hipError_t launch_dequant(const DequantArgs& a, hipStream_t stream);
+
+}  // namespace ep

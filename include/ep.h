@@ -1,0 +1,316 @@
+/*
+ * ep.h -- C ABI of libep: MoE expert-parallel dispatch and combine on one
+ * AMD Instinct MI355X (gfx950), with the EP ranks of a multi-node job laid
+ * out as buffer partitions in the GPU's own HBM.
+ *
+ * The API follows the two-level resource model and the call sequence of
+ * NCCL-EP ("NCCL EP paper notes", lpnh.cn: core functions, tensor
+ * abstraction and tensor layouts): a group created once per model holds the
+ * algorithm mode and all communication buffers; a handle created per forward
+ * pass from topk_idx holds the routing state shared by the matching dispatch
+ * and combine.  The data path is DeepEP's ("NVSHMEM and DeepEP: GPU-initiated
+ * communication"): node-limited routing, FP8 payload with one fp32 scale per
+ * 128 elements, fixed slots in the low-latency (LL) mode and node-
+ * deduplicated same-position rows followed by an intra-node forward in the
+ * high-throughput (HT) mode, and a BF16 weighted combine.
+ *
+ * Conventions
+ *  - Every pointer inside an ep_tensor_t is a device pointer unless a
+ *    function says otherwise; the caller owns it and keeps it alive until the
+ *    work enqueued on the stream has finished.
+ *  - Every operation is enqueued on the caller's HIP stream (passed as
+ *    ep_stream_t, i.e. a hipStream_t; NULL is the default stream) and returns
+ *    without waiting, except the functions documented as blocking.
+ *  - A group, and every handle made from it, is used from one stream at a
+ *    time; the library takes no locks.
+ *  - Arguments are validated on the host before any HIP call; a rejected call
+ *    enqueues nothing.  Routing entries are checked on the device and
+ *    reported through the group's device error word (ep_get_device_error).
+ *  - Nothing throws, aborts or exits across this boundary.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ----------------------------------------------------------------------- */
+/* Status codes                                                              */
+/* ----------------------------------------------------------------------- */
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARGUMENT = 1, /* bad config, descriptor, handle or size   */
+    EP_ERR_CAPACITY = 2,         /* more tokens than max_tokens_per_rank, or
+                                    no free handle slot                      */
+    EP_ERR_OUT_OF_MEMORY = 3,    /* device allocation (or alloc_fn) failed    */
+    EP_ERR_HIP = 4,              /* a HIP runtime call failed; see
+                                    ep_last_hip_error()                      */
+    EP_ERR_UNSUPPORTED = 5       /* valid but outside this build's limits     */
+} ep_status_t;
+
+/* Algorithm mode, chosen once at group creation (NCCL-EP: the group's
+ * config selects HT or LL). */
+typedef enum { EP_MODE_LL = 0, EP_MODE_HT = 1 } ep_mode_t;
+
+/* Element types (NCCL-EP tensor abstraction: FP32/BF16/FP16/FP8). */
+typedef enum {
+    EP_DTYPE_F32 = 0,
+    EP_DTYPE_BF16 = 1,
+    EP_DTYPE_F16 = 2,
+    EP_DTYPE_FP8_E4M3 = 3, /* OCP E4M3 (max 448, no infinities)          */
+    EP_DTYPE_I32 = 4,
+    EP_DTYPE_U8 = 5        /* raw bytes (packed rows and messages)       */
+} ep_dtype_t;
+
+/* Semantic tag of a tensor (NCCL-EP's tensor tags; the page lists the
+ * device-side receive counter twice, the second read here as the host-side
+ * one). */
+typedef enum {
+    EP_TAG_NONE = 0,
+    EP_TAG_TOKENS = 1,
+    EP_TAG_TOPK_IDX = 2,
+    EP_TAG_TOPK_WEIGHTS = 3,
+    EP_TAG_SCALES = 4,
+    EP_TAG_RECV_EXPERT_COUNTER_DEVICE = 5,
+    EP_TAG_RECV_EXPERT_COUNTER_HOST = 6,
+    EP_TAG_TOKENS_PER_EXPERT = 7
+} ep_tensor_tag_t;
+
+/* Bits of the device error word. */
+#define EP_DEVERR_BAD_INDEX 1  /* a topk_idx entry outside [0, num_experts)  */
+#define EP_DEVERR_DUP_INDEX 2  /* a topk_idx entry repeating an earlier one  */
+#define EP_DEVERR_ROW_RANGE 4  /* combine: a row beyond expert_out's rows    */
+
+/* An n-dimensional tensor descriptor (NCCL-EP's ncclNDTensor_t): element
+ * type, up to 3 dimensions, strides in ELEMENTS, and a semantic tag.  The
+ * innermost dimension must be contiguous (stride 1) and data 16-byte
+ * aligned wherever a function says so. */
+typedef struct {
+    void *data;
+    int32_t dtype;       /* ep_dtype_t      */
+    int32_t ndim;        /* 1..3            */
+    int64_t sizes[3];
+    int64_t strides[3];
+    int32_t tag;         /* ep_tensor_tag_t */
+} ep_tensor_t;
+
+/* A hipStream_t. */
+typedef void *ep_stream_t;
+
+/* Group configuration (NCCL-EP group config: mode, number of experts,
+ * maximum tokens per rank, buffer sizing, custom allocator hooks).
+ *
+ * Topology: num_nodes x ranks_per_node EP ranks; rank r sits on node
+ * r / ranks_per_node; expert e lives on rank e / (num_experts / R).  The
+ * first num_src_ranks ranks are the sources whose tokens this GPU routes,
+ * dispatches and combines (token i of a [num_src_ranks * T] batch belongs to
+ * source rank i / T). */
+typedef struct {
+    int32_t mode;                /* ep_mode_t                                  */
+    int32_t num_nodes;           /* N                                          */
+    int32_t ranks_per_node;      /* G                                          */
+    int32_t num_experts;         /* E, divisible by N*G                        */
+    int32_t top_k;               /* K, 1..32                                   */
+    int32_t max_nodes_per_token; /* M; 0 (or >= N) = no node limit             */
+    int32_t hidden;              /* H, multiple of 128 for FP8, of 16 for BF16 */
+    int32_t max_tokens_per_rank; /* T_max: LL slots per (expert, source)       */
+    int32_t num_src_ranks;       /* S, 1..R                                    */
+    int32_t payload;             /* EP_DTYPE_FP8_E4M3 or EP_DTYPE_BF16         */
+    int32_t max_handles;         /* live handles at once; 0 means 2            */
+    int32_t num_cus;             /* cap on CUs used by dispatch/combine; 0=all */
+    /* Optional allocator hooks: both or neither.  alloc_fn returns device
+     * memory of at least `bytes` bytes aligned to 256, or NULL. */
+    void *(*alloc_fn)(size_t bytes, void *ctx);
+    void (*free_fn)(void *ptr, void *ctx);
+    void *alloc_ctx;
+} ep_config_t;
+
+typedef struct ep_group *ep_group_t;
+typedef struct ep_handle *ep_handle_t;
+
+/* ----------------------------------------------------------------------- */
+/* Resources                                                                 */
+/* ----------------------------------------------------------------------- */
+
+/* Create a group (NCCL-EP ncclEpCreateGroup).  Validates the configuration
+ * and allocates, once, every buffer the hot path writes, so that no call
+ * below allocates device memory:
+ *   LL: the fixed-slot receive space, expert-major, E x S x T_max messages
+ *       of (row + 16) bytes; rank r's partition is experts
+ *       [r*E/R, (r+1)*E/R), i.e. a contiguous [E/R][S][T_max] block.
+ *   HT: stage-1 rows (one per token and destination node) and stage-2 rows
+ *       (one per token and expert), each with structure-of-arrays metadata,
+ *       sized for the worst case S*T_max tokens.
+ *   Per handle slot: routing maps and counters for S*T_max tokens.
+ * `stream` orders the initialisation.  On failure nothing stays allocated.
+ * Errors: EP_ERR_INVALID_ARGUMENT (NULL pointers, inconsistent topology,
+ * hidden not a multiple of 128 with FP8, only one allocator hook),
+ * EP_ERR_UNSUPPORTED (E > 1024, K > 32, N > 64, hidden > 16384 or
+ * num_src_ranks > R), EP_ERR_OUT_OF_MEMORY, EP_ERR_HIP. */
+ep_status_t ep_create_group(const ep_config_t *config, ep_stream_t stream,
+                            ep_group_t *out);
+
+/* Free a group and everything it owns (NCCL-EP ncclEpGroupDestroy).  Blocks
+ * until the device is idle.  Handles made from it become invalid. */
+ep_status_t ep_destroy_group(ep_group_t group);
+
+/* Bytes of device memory the group holds. */
+ep_status_t ep_group_memory(ep_group_t group, int64_t *bytes);
+
+/* ----------------------------------------------------------------------- */
+/* Routing (A1)                                                              */
+/* ----------------------------------------------------------------------- */
+
+/* Node-limited top-k routing ("NVSHMEM and DeepEP", high-throughput section:
+ * score every node by the sum of its best ceil(K/M) expert scores -- the best
+ * 2 at K=8, M=4 --, keep the M best nodes, pick the K best experts in them).
+ *   scores   : F32 [n, E], row stride >= E, tag TOKENS or NONE.
+ *   topk_idx : I32 [n, K] out, contiguous, tag TOPK_IDX or NONE.
+ * Ties go to the lower node index and then to the lower expert index; the
+ * K experts of a token are written in descending score order.  Node sums
+ * are float32, largest term first.  n may be 0.  NaN scores are outside the
+ * contract. */
+ep_status_t ep_route(ep_group_t group, const ep_tensor_t *scores,
+                     ep_tensor_t *topk_idx, ep_stream_t stream);
+
+/* ----------------------------------------------------------------------- */
+/* Handles (A2: counts, prefix sums, slot and row maps)                      */
+/* ----------------------------------------------------------------------- */
+
+/* Build the routing state of one forward pass (NCCL-EP ncclEpCreateHandle)
+ * from topk_idx: I32 [n, K] contiguous with n = S*T, T <= T_max.  Token i
+ * belongs to source rank s = i / T and is token t = i % T of it.
+ *   LL: counts[e][s] and slot(i,k) = number of earlier entries (t ascending,
+ *       then k) of the same source with the same expert.
+ *   HT: stage-1 rows: one per (token, distinct destination node n), sent to
+ *       the same-position rank d = n*G + s%G; rows grouped by d, ordered by
+ *       (s, t) inside d.  Stage-2 rows: one per (token, k), grouped by expert
+ *       (hence by rank and local expert), ordered by (s, t) inside an expert.
+ * Entries outside [0,E) or repeating an earlier entry of the same token get
+ * no slot/row (-1) and set a device error bit.  The handle's storage comes
+ * from the group; nothing is allocated.
+ * Errors: EP_ERR_CAPACITY (T > T_max or all handle slots in use),
+ * EP_ERR_INVALID_ARGUMENT. */
+ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t *topk_idx,
+                             ep_stream_t stream, ep_handle_t *out);
+
+/* Return the handle's storage to the group (NCCL-EP ncclEpHandleDestroy).
+ * Stream-ordered reuse: work already enqueued with the handle may still run. */
+ep_status_t ep_destroy_handle(ep_handle_t handle);
+
+/* Rows received by `rank` (NCCL-EP ncclEpHandleGetNumRecvTokens).  BLOCKING:
+ * waits for the handle's stream work and copies the counts to the host --
+ * the HT mode's CPU synchronisation.  rank = -1 gives the total.
+ *   LL: messages in the rank's slots (over its experts and all sources).
+ *   HT: stage-2 rows of the rank.  */
+ep_status_t ep_handle_get_num_recv(ep_handle_t handle, int32_t rank, int64_t *n);
+
+/* Views of the handle's device arrays (read-only for the caller). */
+typedef enum {
+    EP_MAP_LL_SLOT = 0,   /* I32 [n, K]: global slot (e*S+s)*T_max + slot, or -1 */
+    EP_MAP_LL_COUNT = 1,  /* I32 [E, S]                                          */
+    EP_MAP_HT_NODE_ROW = 2, /* I32 [n, N]: global stage-1 row, or -1            */
+    EP_MAP_HT_ROW = 3,    /* I32 [n, K]: global stage-2 row, or -1               */
+    EP_MAP_HT_RANK_COUNT = 4,  /* I32 [R]: stage-1 rows per destination rank    */
+    EP_MAP_HT_RANK_OFFSET = 5, /* I32 [R]: exclusive prefix sum of the above    */
+    EP_MAP_HT_EXPERT_COUNT = 6,  /* I32 [E]: stage-2 rows per expert            */
+    EP_MAP_HT_EXPERT_OFFSET = 7  /* I32 [E]: exclusive prefix sum of the above  */
+} ep_map_t;
+ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *view);
+
+/* ----------------------------------------------------------------------- */
+/* Dispatch (A3 quantise + A4 LL pack | A5 HT stage 1 + A6 HT stage 2)       */
+/* ----------------------------------------------------------------------- */
+
+/* Send every token to its experts (NCCL-EP ncclEpDispatch) -- here: write
+ * it into the group's receive partitions.
+ *   tokens : BF16 [n, H] (n as in the handle), rows 16-byte aligned; or
+ *            FP8_E4M3 [n, H] together with
+ *   scales : F32 [n, H/128] (tag SCALES) -- already quantised tokens are
+ *            packed as they are.  NULL when tokens are BF16.
+ *   topk_weights : optional F32 [n, K]; HT forwards it in the stage-1
+ *            metadata.  Ignored in LL.
+ *   recv_counts  : optional I32 out, tag TOKENS_PER_EXPERT: LL [E, S]
+ *            counts per (expert, source); HT [E] stage-2 rows per expert.
+ * With an FP8 payload each 128-element block is quantised as
+ *   scale = amax/448 (fp32 division), q = E4M3(x/scale) (fp32 division,
+ *   nearest-even, saturating), amax == 0 -> scale 0 and codes 0;
+ * row = [q: H bytes][scales: H/128 fp32] (7392 B at H = 7168).  A BF16
+ * payload row is the H bf16 values (14336 B).
+ *   LL message = row + 16-byte header int32 {src_token, src_rank, k, 0}
+ *     (7408 / 14352 B), stored at message index (e*S + s)*T_max + slot.
+ *   HT stage 1: row at node_row(i,n), metadata per row: src_token, src_rank,
+ *     topk_idx[K], topk_weights[K].  HT stage 2: row at row(i,k), metadata
+ *     per row: src_rank, src_token, k.
+ * Stale contents beyond the counts are left in place (never cleared). */
+ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t *tokens,
+                        const ep_tensor_t *scales, const ep_tensor_t *topk_weights,
+                        ep_tensor_t *recv_counts, ep_stream_t stream);
+
+/* Group-owned receive buffers, as U8/I32/F32 views (device memory). */
+typedef enum {
+    EP_BUF_LL_RECV = 0,        /* U8 [E*S*T_max, row+16]                     */
+    EP_BUF_HT_STAGE1 = 1,      /* U8 [rows1_max, row]                         */
+    EP_BUF_HT_STAGE1_TOKEN = 2,  /* I32 [rows1_max]                           */
+    EP_BUF_HT_STAGE1_SRC = 3,    /* I32 [rows1_max]                           */
+    EP_BUF_HT_STAGE1_TOPK = 4,   /* I32 [rows1_max, K]                        */
+    EP_BUF_HT_STAGE1_WEIGHTS = 5, /* F32 [rows1_max, K]                       */
+    EP_BUF_HT_STAGE2 = 6,      /* U8 [S*T_max*K, row]                         */
+    EP_BUF_HT_STAGE2_SRC = 7,    /* I32 [S*T_max*K]                           */
+    EP_BUF_HT_STAGE2_TOKEN = 8,  /* I32 [S*T_max*K]                           */
+    EP_BUF_HT_STAGE2_K = 9       /* I32 [S*T_max*K]                           */
+} ep_buffer_t;
+ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
+
+/* ----------------------------------------------------------------------- */
+/* Combine (A7)                                                              */
+/* ----------------------------------------------------------------------- */
+
+/* Gather each token's K expert outputs and reduce them in the original token
+ * order (NCCL-EP ncclEpCombine; "NVSHMEM and DeepEP": combine stays BF16):
+ *   out[i][h] = bf16_rne( fma chain over k = 0..K-1 from +0 of
+ *                         w[i][k] * Y[row(i,k)][h] )   in fp32,
+ * where row(i,k) is the LL message index or the HT stage-2 row of the
+ * handle; invalid entries contribute nothing.
+ *   expert_out   : BF16 [rows, H] (or [E, S*T_max, H] in LL), innermost
+ *                  contiguous, rows 16-byte aligned.  A row index >= rows
+ *                  sets EP_DEVERR_ROW_RANGE and is skipped.
+ *   topk_weights : F32 [n, K] contiguous.
+ *   out          : BF16 [n, H], innermost contiguous, rows 16-byte aligned. */
+ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t *expert_out,
+                       const ep_tensor_t *topk_weights, ep_tensor_t *out,
+                       ep_stream_t stream);
+
+/* ----------------------------------------------------------------------- */
+/* Identity expert (test aid and debugging)                                  */
+/* ----------------------------------------------------------------------- */
+
+/* Turn packed rows back into BF16 rows: y = bf16_rne(decode(q) * scale) for
+ * an FP8 payload (one fp32 multiply), a plain copy for a BF16 payload.
+ *   rows : U8 [n, >= row bytes] with the group's payload layout.
+ *   y    : BF16 [n, H].  */
+ep_status_t ep_dequantize_rows(ep_group_t group, const ep_tensor_t *rows,
+                               ep_tensor_t *y, ep_stream_t stream);
+
+/* ----------------------------------------------------------------------- */
+/* Errors                                                                    */
+/* ----------------------------------------------------------------------- */
+
+const char *ep_status_string(ep_status_t status);
+
+/* BLOCKING: wait for the device, return the group's device error bits
+ * (EP_DEVERR_*) accumulated since the last call, and clear them. */
+ep_status_t ep_get_device_error(ep_group_t group, int32_t *code);
+
+/* The last hipError_t seen by this thread inside the library (0 = none). */
+int ep_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

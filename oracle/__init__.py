@@ -223,9 +223,13 @@ def pack_ll(x_bits: np.ndarray, tokens_per_src: int, top_k: int, fp8: bool,
 
 def pack_ht(x_bits, topk, weights, tokens_per_src, num_nodes, fp8, node_row, row2,
             rows1, rows2, with_payload=True):
+    """HT stage-1/stage-2 rows and metadata.  With with_payload=False only the
+    metadata is produced and x_bits may be any [*, H] array (unused)."""
     x = _c(x_bits, np.uint16)
-    n, H = x.shape
-    K = topk.shape[1]
+    H = x.shape[1]
+    n, K = topk.shape
+    if with_payload and x.shape[0] != n:
+        raise ValueError("x must hold every token when payload rows are produced")
     rb = row_bytes(H, fp8)
     out = dict(
         stage1=np.zeros((rows1, rb), np.uint8) if with_payload else None,

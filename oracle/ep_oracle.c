@@ -394,7 +394,8 @@ void orc_pack_ll(const uint16_t *x, int64_t n_tok, int T, int H, int K, int fp8,
  * valid k), with their structure-of-arrays metadata:
  *   stage 1: meta1_tok[row]=t, meta1_src[row]=s, meta1_topk[row*K..]=topk_idx
  *            of the token, meta1_w[row*K..]=topk_weights (if w != NULL)
- *   stage 2: meta2_src[row]=s, meta2_tok[row]=t, meta2_k[row]=k            */
+ *   stage 2: meta2_src[row]=s, meta2_tok[row]=t, meta2_k[row]=k
+ * With both stage pointers NULL only the metadata is produced (x unused). */
 void orc_pack_ht(const uint16_t *x, const int32_t *topk, const float *w,
                  int64_t n_tok, int T, int H, int K, int N, int fp8,
                  const int32_t *node_row, const int32_t *row2,
@@ -407,7 +408,7 @@ void orc_pack_ht(const uint16_t *x, const int32_t *topk, const float *w,
     uint8_t *img = malloc((size_t)row_bytes);
     for (int64_t i = 0; i < n_tok; ++i) {
         const int32_t t = (int32_t)(i % T), s = (int32_t)(i / T);
-        orc_token_row(x + i * H, H, fp8, img);
+        if (stage1 || stage2) orc_token_row(x + i * H, H, fp8, img);
         for (int n = 0; n < N; ++n) {
             int32_t r = node_row[i * N + n];
             if (r < 0) continue;

@@ -1,0 +1,540 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bit-exact for routing, counts, offsets, slot and row maps, FP8 codes, scales,
+headers and metadata; the combine is compared bit for bit as well (the
+stated tolerance, 1e-3 relative per element, is checked alongside and is
+implied by equality).  Full-size workloads compare everything the oracle can
+produce quickly and sample the rest (the rows of a few hundred tokens).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import A, I, bits_of, buffer, dev, ep, get_map, group_for, host, need_gpu, route_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+    yield
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# A1 routing
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("wname", ["ht_prefill", "ll_decode", "round_trip", "tiny"])
+def test_route_full_workloads(wname):
+    w = I.WORKLOADS[wname]
+    say(f"route {wname} n={w.num_tokens}")
+    scores = I.scores_for(w)
+    g = group_for(w, mode="ht", max_tokens_per_rank=w.tokens_per_rank, num_src_ranks=w.num_src_ranks)
+    try:
+        got = route_gpu(g, scores, w.top_k)
+        want = oracle.route(scores, w.num_nodes, w.top_k, w.max_nodes)
+        np.testing.assert_array_equal(got, want)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("E,N,G,K,M,n", [
+    (64, 4, 2, 4, 2, 1001), (128, 8, 2, 6, 3, 257), (512, 8, 8, 8, 4, 300),
+    (1024, 16, 4, 16, 5, 130), (32, 2, 2, 1, 1, 65), (256, 8, 8, 8, 0, 3), (16, 2, 2, 2, 0, 1),
+    (256, 8, 8, 32, 8, 77),
+])
+def test_route_shapes_and_ties(E, N, G, K, M, n):
+    say(f"route E={E} N={N} K={K} M={M} n={n}")
+    rng = np.random.default_rng(E + K + n)
+    scores = (rng.integers(0, 6, size=(n, E)) * 0.125).astype(np.float32)  # many ties
+    scores[::3] = rng.random((len(scores[::3]), E)).astype(np.float32)
+    g = ep.ep_create_group(mode="ht", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=128, max_tokens_per_rank=max(n, 1),
+                           num_src_ranks=1, payload="fp8")
+    try:
+        np.testing.assert_array_equal(route_gpu(g, scores, K), oracle.route(scores, N, K, M))
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_route_empty_and_strided():
+    g = ep.ep_create_group(mode="ht", max_tokens_per_rank=64)
+    try:
+        ep.ep_route(g, torch.empty((0, 256), device="cuda"), torch.empty((0, 8), dtype=torch.int32, device="cuda"))
+        wide = dev(I.uniform_scores(33, 300, seed=3).astype(np.float32))
+        s = wide[:, 7:263]                      # row stride 300, inner contiguous
+        out = torch.empty((33, 8), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, s, out)
+        want = oracle.route(host(s.contiguous()), 8, 8, 4)
+        np.testing.assert_array_equal(host(out), want)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+# ---------------------------------------------------------------------------
+# A2 layout (handle maps)
+# ---------------------------------------------------------------------------
+
+def _ll_case(S, T, E, K, slots, seed, N=8, G=8, corrupt=False):
+    topk = I.random_topk(S * T, E, K, seed)
+    if corrupt:
+        topk[3, 1] = E + 5
+        topk[10, 2] = topk[10, 0]
+        topk[-1, 0] = -1
+    g = ep.ep_create_group(mode="ll", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=0, hidden=128, max_tokens_per_rank=slots,
+                           num_src_ranks=S, payload="fp8")
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        slot = get_map(h, A.EP_MAP_LL_SLOT)
+        cnt = get_map(h, A.EP_MAP_LL_COUNT)
+        err = ep.ep_get_device_error(g)
+        want_cnt, want_slot, want_err = oracle.layout_ll(topk, S, E, slots)
+        np.testing.assert_array_equal(slot, want_slot)
+        np.testing.assert_array_equal(cnt, want_cnt)
+        assert err == want_err
+        n_recv = ep.ep_handle_get_num_recv(h, -1)
+        assert n_recv == want_cnt.sum()
+        L = E // (N * G)
+        assert ep.ep_handle_get_num_recv(h, 1) == want_cnt[L:2 * L].sum()
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("S,T,E,K,slots", [
+    (64, 128, 256, 8, 128), (1, 128, 256, 8, 128), (3, 300, 256, 8, 512), (5, 1000, 64, 4, 1000),
+    (2, 17, 128, 12, 20), (1, 1, 256, 8, 8), (4, 257, 1024, 32, 300),
+])
+def test_layout_ll(S, T, E, K, slots):
+    say(f"layout LL S={S} T={T} E={E} K={K}")
+    _ll_case(S, T, E, K, slots, seed=S * 1000 + T)
+
+
+def test_layout_ll_invalid_entries():
+    _ll_case(2, 40, 64, 4, 64, seed=9, corrupt=True)
+
+
+def _ht_compare(topk, S, E, N, G, T_max=None):
+    T = topk.shape[0] // S
+    g = ep.ep_create_group(mode="ht", num_nodes=N, ranks_per_node=G, num_experts=E,
+                           top_k=topk.shape[1], max_nodes_per_token=0, hidden=128,
+                           max_tokens_per_rank=T_max or max(T, 1), num_src_ranks=S, payload="fp8")
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        want = oracle.layout_ht(topk, S, E, N, G)
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_NODE_ROW), want["node_row"])
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_ROW), want["row2"])
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_RANK_COUNT), want["c1"])
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_RANK_OFFSET), want["off1"])
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_EXPERT_COUNT), want["c2"])
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_EXPERT_OFFSET), want["off2"])
+        assert ep.ep_get_device_error(g) == want["err"]
+        L = E // (N * G)
+        assert ep.ep_handle_get_num_recv(h, 2) == want["c2"][2 * L:3 * L].sum()
+        ep.ep_destroy_handle(h)
+        return want
+    finally:
+        ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("wname", ["ht_prefill", "round_trip"])
+def test_layout_ht_full_workloads(wname):
+    w = I.WORKLOADS[wname]
+    say(f"layout HT {wname}")
+    topk = oracle.route(I.scores_for(w), w.num_nodes, w.top_k, w.max_nodes)
+    want = _ht_compare(topk, 1, w.num_experts, w.num_nodes, w.ranks_per_node)
+    if wname == "ht_prefill":
+        # the page's node-dedup figure: 13,758 cross-node rows = 3.36 per token
+        assert round((want["c1"].sum() - want["c1"][:8].sum()) / 4096, 2) == 3.36
+
+
+@pytest.mark.parametrize("S,T,E,N,G,K", [
+    (4, 32, 16, 2, 2, 2), (3, 600, 256, 8, 8, 8), (8, 77, 64, 4, 2, 5), (1, 1, 256, 8, 8, 8),
+    (16, 300, 128, 4, 4, 16),
+])
+def test_layout_ht_shapes(S, T, E, N, G, K):
+    say(f"layout HT S={S} T={T} E={E} N={N} G={G} K={K}")
+    topk = I.random_topk(S * T, E, K, seed=S + T + E)
+    _ht_compare(topk, S, E, N, G)
+
+
+def test_layout_ht_invalid_entries():
+    topk = I.random_topk(3 * 50, 64, 4, seed=77)
+    topk[0, 0] = 64
+    topk[7, 3] = topk[7, 1]
+    _ht_compare(topk, 3, 64, 4, 2)
+
+
+def test_handle_pool_capacity():
+    g = ep.ep_create_group(mode="ll", num_nodes=2, ranks_per_node=2, num_experts=16, top_k=2,
+                           max_nodes_per_token=0, hidden=128, max_tokens_per_rank=8,
+                           num_src_ranks=1, payload="fp8", max_handles=2)
+    try:
+        t = dev(I.random_topk(8, 16, 2, seed=1))
+        h1 = ep.ep_create_handle(g, t)
+        h2 = ep.ep_create_handle(g, t)
+        with pytest.raises(ep.EpError) as ei:
+            ep.ep_create_handle(g, t)
+        assert ei.value.status == A.EP_ERR_CAPACITY
+        ep.ep_destroy_handle(h1)
+        with pytest.raises(ep.EpError):
+            ep.ep_destroy_handle(h1)             # already destroyed
+        h3 = ep.ep_create_handle(g, t)
+        ep.ep_destroy_handle(h2)
+        ep.ep_destroy_handle(h3)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+# ---------------------------------------------------------------------------
+# A3 + A4: LL dispatch
+# ---------------------------------------------------------------------------
+
+def _ll_dispatch(S, T, E, K, H, payload, slots, seed, N=2, G=2, M=0, sample=None):
+    fp8 = payload == "fp8"
+    x = I.normal_bf16(S * T, H, seed)
+    x[0, :128] = 0.0                              # an all-zero block
+    if H >= 256:
+        x[1, 128:256] = -0.0
+    scores = I.uniform_scores(S * T, E, seed + 1).astype(np.float32)
+    g = ep.ep_create_group(mode="ll", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=H, max_tokens_per_rank=slots,
+                           num_src_ranks=S, payload=payload)
+    try:
+        topk_d = torch.empty((S * T, K), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        h = ep.ep_create_handle(g, topk_d)
+        counts = torch.zeros((E, S), dtype=torch.int32, device="cuda")
+        ep.ep_dispatch(h, x.cuda(), recv_counts=counts)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, N, K, M))
+        want_cnt, want_slot, _ = oracle.layout_ll(topk, S, E, slots)
+        np.testing.assert_array_equal(host(counts), want_cnt)
+        slot = get_map(h, A.EP_MAP_LL_SLOT)
+        np.testing.assert_array_equal(slot, want_slot)
+        buf = buffer(g, A.EP_BUF_LL_RECV)
+        xb = I.bf16_bits(x)
+        toks = np.arange(S * T) if sample is None else sample
+        rows = oracle.token_rows(xb[toks], fp8)
+        rb = rows.shape[1]
+        for j, i in enumerate(toks):
+            got = host(buf[torch.from_numpy(slot[i].astype(np.int64)).cuda()])
+            for k in range(K):
+                np.testing.assert_array_equal(got[k, :rb], rows[j], err_msg=f"token {i} k {k}")
+                assert list(got[k, rb:].view(np.int32)) == [i % T, i // T, k, 0]
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("payload", ["fp8", "bf16"])
+def test_ll_dispatch_tiny(payload):
+    say(f"LL dispatch tiny {payload}")
+    _ll_dispatch(4, 32, 16, 2, 256, payload, 32, seed=1)
+
+
+def test_ll_dispatch_ragged_hidden():
+    say("LL dispatch H=1152 (9 blocks, ragged wave), S=3 T=70")
+    _ll_dispatch(3, 70, 64, 4, 1152, "fp8", 80, seed=5, N=4, G=2, M=2)
+
+
+def test_ll_dispatch_full_decode_shape():
+    """64 sources x 128 tokens, hidden 7168, 8x8 ranks, node-limited top-8."""
+    w = I.LL_DECODE
+    say("LL dispatch full decode shape (sampled rows)")
+    rng = np.random.default_rng(123)
+    sample = np.sort(rng.choice(w.num_tokens, size=96, replace=False))
+    x = I.tokens_for(w)
+    scores = I.scores_for(w)
+    g = group_for(w)
+    try:
+        topk_d = torch.empty((w.num_tokens, 8), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        h = ep.ep_create_handle(g, topk_d)
+        ep.ep_dispatch(h, x.cuda())
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, 8, 8, 4))
+        want_cnt, want_slot, _ = oracle.layout_ll(topk, 64, 256, 128)
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_LL_COUNT), want_cnt)
+        slot = get_map(h, A.EP_MAP_LL_SLOT)
+        np.testing.assert_array_equal(slot, want_slot)
+        buf = buffer(g, A.EP_BUF_LL_RECV)
+        assert buf.shape == (256 * 64 * 128, 7408)
+        rows = oracle.token_rows(I.bf16_bits(x)[sample], True)
+        for j, i in enumerate(sample):
+            got = host(buf[torch.from_numpy(slot[i].astype(np.int64)).cuda()])
+            np.testing.assert_array_equal(got[:, :7392], np.repeat(rows[j:j + 1], 8, axis=0))
+            np.testing.assert_array_equal(got[:, 7392:].view(np.int32),
+                                          [[i % 128, i // 128, k, 0] for k in range(8)])
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+# ---------------------------------------------------------------------------
+# A3 + A5 + A6: HT dispatch
+# ---------------------------------------------------------------------------
+
+def _ht_dispatch(w, x, scores, weights, sample=None, in_fp8=False):
+    S, T, K, H = w.num_src_ranks, w.tokens_per_rank, w.top_k, w.hidden
+    fp8 = w.payload == "fp8"
+    g = group_for(w)
+    try:
+        topk_d = torch.empty((S * T, K), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        h = ep.ep_create_handle(g, topk_d)
+        counts = torch.zeros(w.num_experts, dtype=torch.int32, device="cuda")
+        if in_fp8:
+            q, sc = oracle.quantize_rows(I.bf16_bits(x))
+            xq = torch.from_numpy(q).cuda().view(torch.float8_e4m3fn)
+            ep.ep_dispatch(h, xq, scales=dev(sc), topk_weights=dev(weights), recv_counts=counts)
+        else:
+            ep.ep_dispatch(h, x.cuda(), topk_weights=dev(weights), recv_counts=counts)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, w.num_nodes, K, w.max_nodes))
+        lay = oracle.layout_ht(topk, S, w.num_experts, w.num_nodes, w.ranks_per_node)
+        np.testing.assert_array_equal(host(counts), lay["c2"])
+        node_row = get_map(h, A.EP_MAP_HT_NODE_ROW)
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        np.testing.assert_array_equal(node_row, lay["node_row"])
+        np.testing.assert_array_equal(row2, lay["row2"])
+        rows1, rows2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+        meta = oracle.pack_ht(I.bf16_bits(x[:1]), topk, weights, T, w.num_nodes, fp8,
+                              lay["node_row"], lay["row2"], rows1, rows2, with_payload=False)
+        for name, which in [("meta1_tok", A.EP_BUF_HT_STAGE1_TOKEN), ("meta1_src", A.EP_BUF_HT_STAGE1_SRC),
+                            ("meta1_topk", A.EP_BUF_HT_STAGE1_TOPK), ("meta1_w", A.EP_BUF_HT_STAGE1_WEIGHTS)]:
+            np.testing.assert_array_equal(host(buffer(g, which)[:rows1]), meta[name], err_msg=name)
+        for name, which in [("meta2_src", A.EP_BUF_HT_STAGE2_SRC), ("meta2_tok", A.EP_BUF_HT_STAGE2_TOKEN),
+                            ("meta2_k", A.EP_BUF_HT_STAGE2_K)]:
+            np.testing.assert_array_equal(host(buffer(g, which)[:rows2]), meta[name], err_msg=name)
+        st1 = buffer(g, A.EP_BUF_HT_STAGE1)
+        st2 = buffer(g, A.EP_BUF_HT_STAGE2)
+        toks = np.arange(S * T) if sample is None else sample
+        img = oracle.token_rows(I.bf16_bits(x)[toks], fp8)
+        for j, i in enumerate(toks):
+            r1 = node_row[i][node_row[i] >= 0]
+            r2 = row2[i][row2[i] >= 0]
+            got1 = host(st1[torch.from_numpy(r1.astype(np.int64)).cuda()])
+            got2 = host(st2[torch.from_numpy(r2.astype(np.int64)).cuda()])
+            np.testing.assert_array_equal(got1, np.repeat(img[j:j + 1], len(r1), axis=0), err_msg=f"st1 token {i}")
+            np.testing.assert_array_equal(got2, np.repeat(img[j:j + 1], len(r2), axis=0), err_msg=f"st2 token {i}")
+        ep.ep_destroy_handle(h)
+        return g, topk, lay
+    except BaseException:
+        ep.ep_destroy_group(g)
+        raise
+
+
+def test_ht_dispatch_midsize_all_rows():
+    w = I.HT_PREFILL.with_(tokens_per_rank=700, hidden=1024, seed=31, num_src_ranks=3)
+    say("HT dispatch S=3 T=700 H=1024 (all rows)")
+    x = I.tokens_for(w)
+    g, _, _ = _ht_dispatch(w, x, I.scores_for(w), I.normal_weights(w.num_tokens, 8, 31))
+    ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("payload", ["fp8", "bf16"])
+def test_ht_dispatch_tiny(payload):
+    w = I.TINY.with_(mode="ht", payload=payload)
+    say(f"HT dispatch tiny {payload}")
+    scores = I.scores_for(w)
+    x = I.tokens_for(w)
+    g, _, _ = _ht_dispatch(w, x, scores, I.normal_weights(w.num_tokens, w.top_k, 3))
+    ep.ep_destroy_group(g)
+
+
+def test_ht_dispatch_prequantised_input():
+    w = I.HT_PREFILL.with_(tokens_per_rank=300, hidden=512, seed=41)
+    say("HT dispatch with FP8 input + scales")
+    x = I.tokens_for(w)
+    g, _, _ = _ht_dispatch(w, x, I.scores_for(w), I.normal_weights(300, 8, 41), in_fp8=True)
+    ep.ep_destroy_group(g)
+
+
+def test_ht_dispatch_full_prefill_shape():
+    """The page's shape: 4096 tokens, hidden 7168, seed 0 scores (sampled rows)."""
+    w = I.HT_PREFILL
+    say("HT dispatch full prefill shape (sampled rows)")
+    rng = np.random.default_rng(7)
+    sample = np.sort(rng.choice(w.num_tokens, size=128, replace=False))
+    x = I.tokens_for(w)
+    g, topk, lay = _ht_dispatch(w, x, I.scores_for(w), I.normal_weights(4096, 8, w.seed), sample=sample)
+    try:
+        assert lay["c1"].sum() == 16248 and lay["c2"].sum() == 32768
+    finally:
+        ep.ep_destroy_group(g)
+
+
+# ---------------------------------------------------------------------------
+# A7 combine
+# ---------------------------------------------------------------------------
+
+def test_combine_cfg_geometry_sampled():
+    """4096 tokens x top-8 over 32768 bf16 rows of hidden 7168 (the combine
+    workload); rows placed by the HT handle of the page's routing."""
+    w = I.COMBINE
+    say("combine 4096x8x7168 (sampled tokens)")
+    scores = I.scores_for(w)
+    g = group_for(w)
+    try:
+        topk_d = torch.empty((4096, 8), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        h = ep.ep_create_handle(g, topk_d)
+        Yt = I.normal_bf16(32768, 7168, w.seed)
+        wts = I.normal_weights(4096, 8, w.seed)
+        out = torch.empty((4096, 7168), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(h, Yt.cuda(), dev(wts), out)
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        rng = np.random.default_rng(11)
+        which = np.sort(rng.choice(4096, size=48, replace=False))
+        want = oracle.combine(I.bf16_bits(Yt), wts, row2, which=which)
+        got = host(out)[which]
+        np.testing.assert_array_equal(got, want)
+        assert ep.ep_get_device_error(g) == 0
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("n,K,H", [(1000, 8, 1024), (257, 2, 256), (64, 13, 512), (3, 32, 128)])
+def test_combine_all_tokens(n, K, H):
+    say(f"combine n={n} K={K} H={H}")
+    topk = I.random_topk(n, 4 * K, K, seed=n)
+    g = ep.ep_create_group(mode="ht", num_nodes=1, ranks_per_node=1, num_experts=4 * K, top_k=K,
+                           max_nodes_per_token=0, hidden=H, max_tokens_per_rank=n,
+                           num_src_ranks=1, payload="bf16")
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        Yt = I.normal_bf16(n * K, H, seed=n + 1)
+        wts = I.normal_weights(n, K, seed=n + 2)
+        out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(h, Yt.cuda(), dev(wts), out)
+        want = oracle.combine(I.bf16_bits(Yt), wts, row2)
+        got = host(out)
+        np.testing.assert_array_equal(got, want)
+        # the stated tolerance, for the record (implied by equality)
+        g32 = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float()
+        r32 = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float()
+        assert torch.all((g32 - r32).abs() <= 1e-3 * torch.clamp(r32.abs(), min=1e-3))
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_combine_invalid_and_out_of_range_rows():
+    n, K, H = 40, 4, 256
+    topk = I.random_topk(n, 16, K, seed=3)
+    topk[5, 2] = 99                       # invalid: no row, contributes nothing
+    g = ep.ep_create_group(mode="ht", num_nodes=1, ranks_per_node=1, num_experts=16, top_k=K,
+                           max_nodes_per_token=0, hidden=H, max_tokens_per_rank=n,
+                           num_src_ranks=1, payload="bf16")
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        assert ep.ep_get_device_error(g) == A.EP_DEVERR_BAD_INDEX
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        assert row2[5, 2] == -1
+        rows = n * K - 1
+        Yt = I.normal_bf16(rows, H, seed=4)
+        wts = I.normal_weights(n, K, seed=5)
+        out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        # give fewer rows than the handle addresses: the last row index is out of range
+        short = Yt[: rows - 3].cuda()
+        ep.ep_combine(h, short, dev(wts), out)
+        assert ep.ep_get_device_error(g) == A.EP_DEVERR_ROW_RANGE
+        loc = row2.copy()
+        loc[loc >= rows - 3] = -1
+        np.testing.assert_array_equal(host(out), oracle.combine(I.bf16_bits(Yt[: rows - 3]), wts, loc))
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+# ---------------------------------------------------------------------------
+# Round trips with the identity expert
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("mode", ["ll", "ht"])
+def test_tiny_identity_roundtrip_returns_input(mode):
+    """Tiny workload: 128 tokens, hidden 256, 16 experts on 4 ranks, top-2, no
+    node limit, BF16 payload, identity experts and softmax-normalised weights
+    of the selected scores: the combine returns the input bit for bit."""
+    w = I.TINY.with_(mode=mode)
+    say(f"tiny identity round trip {mode}")
+    scores = I.scores_for(w)
+    x = I.tokens_for(w)
+    g = group_for(w)
+    try:
+        topk_d = torch.empty((128, 2), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, 2, 2, 0))
+        wts = I.weights_for(w, scores, topk)
+        h = ep.ep_create_handle(g, topk_d)
+        ep.ep_dispatch(h, x.cuda(), topk_weights=dev(wts))
+        if mode == "ll":
+            rows = buffer(g, A.EP_BUF_LL_RECV)
+        else:
+            rows = buffer(g, A.EP_BUF_HT_STAGE2)
+        y = torch.empty((rows.shape[0], 256), dtype=torch.bfloat16, device="cuda")
+        ep.ep_dequantize_rows(g, rows, y)
+        out = torch.empty((128, 256), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(h, y, dev(wts), out)
+        np.testing.assert_array_equal(host(out), I.bf16_bits(x))
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_fp8_roundtrip_large_skewed_sampled():
+    """16384 tokens, Zipf(1.1) popularity, FP8 dispatch (HT), identity expert,
+    BF16 combine: sampled tokens equal the oracle's round trip bit for bit and
+    stay within the FP8 error bound of the input."""
+    w = I.ROUND_TRIP
+    say("FP8 round trip 16384 tokens (sampled)")
+    scores = I.scores_for(w)
+    x = I.tokens_for(w)
+    wts_all = None
+    g = group_for(w)
+    try:
+        topk_d = torch.empty((w.num_tokens, 8), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, 8, 8, 4))
+        wts_all = I.weights_for(w, scores, topk)
+        h = ep.ep_create_handle(g, topk_d)
+        ep.ep_dispatch(h, x.cuda(), topk_weights=dev(wts_all))
+        n_rows = ep.ep_handle_get_num_recv(h, -1)
+        assert n_rows == w.num_tokens * 8
+        st2 = buffer(g, A.EP_BUF_HT_STAGE2)[:n_rows]
+        y = torch.empty((n_rows, 7168), dtype=torch.bfloat16, device="cuda")
+        ep.ep_dequantize_rows(g, st2, y)
+        out = torch.empty((w.num_tokens, 7168), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(h, y, dev(wts_all), out)
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        rng = np.random.default_rng(5)
+        which = np.sort(rng.choice(w.num_tokens, size=40, replace=False))
+        rows_needed = np.unique(row2[which].ravel())
+        st2_rows = host(st2[torch.from_numpy(rows_needed.astype(np.int64)).cuda()])
+        y_or = oracle.dequant_rows(st2_rows, 7168, True)
+        # the oracle's own stage-2 rows of those tokens must equal the GPU's
+        img = oracle.token_rows(I.bf16_bits(x)[which], True)
+        pos = {r: j for j, r in enumerate(rows_needed)}
+        for j, i in enumerate(which):
+            for k in range(8):
+                np.testing.assert_array_equal(st2_rows[pos[row2[i, k]]], img[j])
+        remap = np.vectorize(pos.get)(row2[which]).astype(np.int32)
+        want = oracle.combine(y_or, wts_all[which], remap)
+        got = host(out)[which]
+        np.testing.assert_array_equal(got, want)
+        xf = x[which].float().numpy()
+        gf = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
+        amax = np.abs(xf).reshape(len(which), -1, 128).max(axis=2).repeat(128, axis=1)
+        assert np.all(np.abs(gf - xf) <= 2.0**-4 * np.abs(xf) + 2.0**-8 * np.abs(xf) + amax * 2.0**-9 + 1e-6)
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
