@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark: MoE EP dispatch + combine at the 4096-token DeepSeek-V3 shape on one MI355X.
+
+One step = the whole hot path over one batch, all inputs resident in HBM:
+  route    (A1)      scores [4096, 256] f32 -> topk_idx [4096, 8]
+  handle   (A2)      counts, prefix sums, stage-1 node rows, stage-2 rows
+  dispatch (A3+A5+A6) FP8 quantisation, node-deduplicated same-position
+                     stage-1 rows and expert-grouped stage-2 rows (+ metadata)
+  combine  (A7)      32768 expert-output rows (bf16, hidden 7168) gathered,
+                     weighted and reduced back to [4096, 7168] bf16
+Workload: 8 nodes x 8 ranks, 256 experts, top-8, at most 4 nodes per token,
+router scores U[0,1) + 0.5*U[0,1) per expert (seed 0) -- the DeepEP page's
+routing study; tokens and expert outputs ~N(0,1) bf16; weights softmax of
+N(0,1) logits.  Four input sets rotate so that no step reads what the
+previous one left in the last-level cache.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+Prints one JSON line (rank 0).  value = algorithmic bytes of one step /
+step time, in GB/s; tokens/s and the fraction of the 8 TB/s HBM peak are
+reported beside it.  The roofline object describes the dominant kernel with
+its own average duration from HIP events recorded on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import ep_inputs as I  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+N_SETS = 4
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ht_prefill_combine_4096.txt")
+KERNEL_SOURCES = ("ep_dispatch.hip", "ep_combine.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(n_tok, K, H, rows1, rows2, E):
+    """Bytes each step must move at least once (read + write), per kernel.
+
+    route    : scores n*E*4 read, topk n*K*4 written
+    handle   : topk n*K*4 read; node rows n*N*4 and stage-2 rows n*K*4 written
+               (counted under dispatch in the headline total, as read there)
+    dispatch : tokens n*H*2 read, topk + weights 2*n*K*4 read,
+               stage-1 rows1*(H + H/128*4) + metadata rows1*(2 + 2K)*4,
+               stage-2 rows2*(H + H/128*4) + metadata rows2*3*4 written
+    combine  : rows2*H*2 read, weights n*K*4 + row map n*K*4 read,
+               n*H*2 written
+    """
+    row = H + H // 128 * 4
+    route = n_tok * E * 4 + n_tok * K * 4
+    dispatch = (n_tok * H * 2 + 2 * n_tok * K * 4 + rows1 * row + rows1 * (2 + 2 * K) * 4
+                + rows2 * row + rows2 * 3 * 4)
+    combine = rows2 * H * 2 + 2 * n_tok * K * 4 + n_tok * H * 2
+    # headline total = scores + tokens + topk + weights + stage rows/meta + combine
+    total = n_tok * E * 4 + dispatch + combine
+    return dict(route=route, dispatch=dispatch, combine=combine, total=total)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "combine_ep_route_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(kernel: str):
+    """HBM bytes per launch measured with rocprofv3 PMC counters, if the
+    stored measurement was taken on the current kernel sources."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("source_sha256_16") != source_digest():
+        return None
+    v = vals.get(f"{kernel}_bytes_per_launch")
+    return float(v) if v else None
+
+
+def cpu_baseline(scores, x, weights, Y, n_tok):
+    """The oracle on the same workload (all 4096 tokens), single thread."""
+    import oracle
+    xb = I.bf16_bits(x)
+    yb = I.bf16_bits(Y)
+    t0 = time.perf_counter()
+    topk = oracle.route(scores, 8, 8, 4)
+    lay = oracle.layout_ht(topk, 1, 256, 8, 8)
+    rows1, rows2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+    oracle.pack_ht(xb, topk, weights, n_tok, 8, True, lay["node_row"], lay["row2"], rows1, rows2)
+    oracle.combine(yb, weights, lay["row2"])
+    dt = time.perf_counter() - t0
+    b = algorithmic_bytes(n_tok, 8, 7168, rows1, rows2, 256)["total"]
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"the whole step workload once ({n_tok} tokens: route, layout, "
+                       f"FP8 quantise + HT pack, combine), {dt:.2f} s single-threaded",
+                seconds=round(dt, 3), tokens_per_s=round(n_tok / dt, 1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--num-cus", type=int, default=0, help="CU cap for dispatch/combine (0 = all)")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    import combine_ep_route_amd as ep
+
+    w = I.HT_PREFILL
+    n_tok, E, K, H = w.num_tokens, w.num_experts, w.top_k, w.hidden
+    log(f"[bench] building inputs: {n_tok} tokens, hidden {H}, {E} experts, top-{K}")
+    scores = I.scores_for(w)
+    x = I.tokens_for(w)
+    weights = I.normal_weights(n_tok, K, w.seed)
+    Y = I.normal_bf16(n_tok * K, H, I.COMBINE.seed)
+
+    dev = torch.device("cuda")
+    sets = []
+    for j in range(N_SETS):
+        # every set holds the same values in different memory
+        sets.append(dict(scores=torch.from_numpy(scores).to(dev), x=x.to(dev),
+                         topk=torch.empty((n_tok, K), dtype=torch.int32, device=dev),
+                         out=torch.empty((n_tok, H), dtype=torch.bfloat16, device=dev)))
+    w_d = torch.from_numpy(weights).to(dev)
+    Y_d = Y.to(dev)
+
+    g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
+                           max_nodes_per_token=4, hidden=H, max_tokens_per_rank=n_tok,
+                           num_src_ranks=1, payload="fp8", num_cus=args.num_cus)
+    stream = torch.cuda.current_stream()
+
+    def step(j, ev=None):
+        s = sets[j % N_SETS]
+        if ev is not None:
+            ev[0].record(stream)
+        ep.ep_route(g, s["scores"], s["topk"])
+        if ev is not None:
+            ev[1].record(stream)
+        h = ep.ep_create_handle(g, s["topk"])
+        if ev is not None:
+            ev[2].record(stream)
+        ep.ep_dispatch(h, s["x"], topk_weights=w_d)
+        if ev is not None:
+            ev[3].record(stream)
+        ep.ep_combine(h, Y_d, w_d, s["out"])
+        if ev is not None:
+            ev[4].record(stream)
+        ep.ep_destroy_handle(h)
+
+    log(f"[bench] warmup {args.warmup}")
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    assert ep.ep_get_device_error(g) == 0
+
+    # Exact row counts of this routing (the same every step).
+    h = ep.ep_create_handle(g, sets[0]["topk"])
+    rows2 = ep.ep_handle_get_num_recv(h, -1)
+    rows1 = int(ep.ep_handle_get_map(h, ep._abi.EP_MAP_HT_RANK_COUNT).sum().item())
+    ep.ep_destroy_handle(h)
+    ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E)
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(j, events[j])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    assert ep.ep_get_device_error(g) == 0
+
+    per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(4)]
+                    for j in range(args.steps)])  # ms
+    mean_ms = per.mean(axis=0)
+    names = ["route", "handle", "dispatch", "combine"]
+    ms_per_step = wall * 1e3 / args.steps
+    value = ab["total"] / (ms_per_step * 1e-3) / 1e9
+
+    dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
+    dom_ms = mean_ms[names.index(dom)]
+    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
+    traffic = stored_traffic(dom)
+
+    result = {
+        "metric": "dispatch+combine HBM GB/s and tokens/s on 1 MI355X (% of HBM peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 payload / bf16 combine, fp32 accumulate",
+        "data": "synthetic (seeded; page-3 score distribution, N(0,1) tokens and expert outputs)",
+        "config": {"workload": "ht_prefill_4096_plus_combine", "tokens": n_tok, "hidden": H,
+                   "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
+                   "max_nodes_per_token": 4, "stage1_rows": rows1, "stage2_rows": rows2,
+                   "algorithmic_bytes_per_step": ab["total"]},
+        "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": {k: round(float(v), 5) for k, v in zip(names, mean_ms)},
+        "kernel_gbs": {"route": round(ab["route"] / (mean_ms[0] * 1e-3) / 1e9, 1),
+                       "dispatch": round(ab["dispatch"] / (mean_ms[2] * 1e-3) / 1e9, 1),
+                       "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom]},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on the same workload")
+        cb = cpu_baseline(scores, x, weights, Y, n_tok)
+        result["cpu_baseline"] = cb
+    ep.ep_destroy_group(g)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
