@@ -121,6 +121,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--num-cus", type=int, default=0, help="CU cap for dispatch/combine (0 = all)")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="graph: the step is captured once per input set in a HIP graph and replayed; "
+                         "eager: every step is enqueued from Python")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
@@ -186,21 +189,51 @@ def main(argv=None):
     ep.ep_destroy_handle(h)
     ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E)
 
+    # Eager pass with events around every call: per-kernel durations.
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps")
+    log(f"[bench] eager: timing {args.steps} steps with per-call events")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for j in range(args.steps):
         step(j, events[j])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    wall_eager = time.perf_counter() - t0
     assert ep.ep_get_device_error(g) == 0
-
     per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(4)]
                     for j in range(args.steps)])  # ms
     mean_ms = per.mean(axis=0)
     names = ["route", "handle", "dispatch", "combine"]
-    ms_per_step = wall * 1e3 / args.steps
+    ms_eager = wall_eager * 1e3 / args.steps
+
+    ms_per_step = ms_eager
+    if args.mode == "graph":
+        # One graph holds one step per input set; a replay runs N_SETS steps.
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step(0)            # warm the capture stream
+        torch.cuda.current_stream().wait_stream(cap)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=cap):
+            for j in range(N_SETS):
+                step(j)
+        reps = max(1, args.steps // N_SETS)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] graph: timing {reps * N_SETS} steps ({reps} replays)")
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * N_SETS)
+        assert ep.ep_get_device_error(g) == 0
+        # the graph's output equals the eager output of the same step
+        ref = sets[0]["out"].clone()
+        step(0)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int16), sets[0]["out"].view(torch.int16))
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
 
     dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
@@ -216,6 +249,8 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "execution": args.mode,
+        "ms_per_step_eager": round(ms_eager, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -11,8 +11,9 @@
 // Mapping: grid (column blocks, tokens); the token index comes from
 // blockIdx.y, so its K row indices and weights are scalar loads.  Thread c
 // owns 8 bf16 (16 bytes) of the row; it issues the K gathered 16-byte loads
-// before the first multiply-add so that K loads per lane are in flight, then
-// runs the fp32 fma chain in k order and stores 16 bytes of bf16.
+// (non-temporal: every expert-output row is read exactly once) before the
+// first multiply-add so that K loads per lane are in flight, then runs the
+// fp32 fma chain in k order and stores 16 bytes of bf16.
 #include "ep_internal.h"
 
 namespace ep {
@@ -51,8 +52,10 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         ok[b] = r >= 0 && r < a.rows;
         wk[b] = k < a.K ? a.w[i * a.K + k] : 0.0f;
         if (r >= a.rows && c == 0) atomicOr(a.err, EP_DEVERR_ROW_RANGE);
+        // each expert-output row is read exactly once: stream it past the caches
         v[b] = (ok[b] && active)
-                   ? *reinterpret_cast<const u32x4*>(a.y + static_cast<int64_t>(r) * a.ld_y + 8 * c)
+                   ? __builtin_nontemporal_load(
+                         reinterpret_cast<const u32x4*>(a.y + static_cast<int64_t>(r) * a.ld_y + 8 * c))
                    : u32x4{0, 0, 0, 0};
       }
 #pragma unroll

@@ -1,21 +1,30 @@
-// A3 + A4 / A5 + A6: quantise each token once and write its row to every
-// destination the handle assigned (LL messages, HT stage-1 and stage-2 rows).
+// A3 + A4 / A5 + A6: for each token, finish its slots / rows from the
+// handle's tile prefix sums, quantise it once and write its row to every
+// destination (LL messages, HT stage-1 and stage-2 rows).
 //
 // Sources: "NVSHMEM and DeepEP: GPU-initiated communication" -- FP8 dispatch
 // with one fp32 scale per 128 elements (7168 + 56*4 bytes per token), LL
-// message = payload + scales + 16-byte header (7408 B), HT one copy per
-// destination node at the same-position GPU followed by the intra-node
-// forward; "NCCL EP paper notes" -- quantisation inside the send kernel's
-// prepare stage, message sizes 7408 B (FP8) / 14352 B (BF16).
+// message = payload + scales + 16-byte header (7408 B), fixed slots per
+// (local expert, source rank), HT one copy per destination node at the
+// same-position GPU followed by the intra-node forward; "NCCL EP paper
+// notes" -- quantisation inside the send kernel's prepare stage, message
+// sizes 7408 B (FP8) / 14352 B (BF16).
 //
-// Mapping: one workgroup per token (grid-stride when the CU cap is set);
-// thread c owns elements [16c, 16c+16): two 16-byte loads of bf16, and one
-// 16-byte store of FP8 codes per destination row.  A 128-element block is 8
-// consecutive lanes, so its amax is a 3-step xor-shuffle inside a DPP row.
-// The destination list of a token is workgroup-uniform (scalar loads).  The
-// source row is read once and the quantised chunk stays in registers for all
-// destinations; rows are written with non-temporal stores because nothing
-// on this GPU reads them back before the next pass.
+// Mapping: one workgroup per token (grid-stride when a CU cap is set).
+//  1. Thread c issues the loads of elements [16c, 16c+16) (two 16-byte
+//     loads of bf16) first, so they are in flight during step 2.
+//  2. Wave 0 ranks the token inside its 64-token tile: lane l looks at the
+//     l-th earlier token of the tile, and one ballot per expert (and per
+//     destination node) counts the earlier tokens that share it.  Adding the
+//     tile's prefix from the handle gives the slot / row of every entry; the
+//     positions are workgroup-uniform and kept in scalar registers.
+//  3. A 128-element block is 8 consecutive lanes; its amax is a 3-step
+//     xor-shuffle inside a DPP row.  scale = amax/448 and q = E4M3(x/scale),
+//     both IEEE fp32 divisions (round to nearest even).
+//  4. The 16-byte chunk of codes is stored to every destination row with
+//     non-temporal stores (nothing on this GPU reads the rows back during
+//     the pass); each half-wave writes its 4 block scales with one 16-byte
+//     store.
 #include "ep_internal.h"
 
 namespace ep {
@@ -23,6 +32,8 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kTile = kLayoutTile;
 
 // E4M3 (OCP, max 448) from fp32: nearest, ties to even, saturating, sign of
 // zero kept.  Normal range: round the fp32 mantissa to 3 bits at bit 20
@@ -50,140 +61,269 @@ __device__ __forceinline__ void store_nt(u32x4 v, uint8_t* p) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
 }
 
-// One token's chunk, ready to store: FP8 codes (16 B) or BF16 (32 B).
-struct Chunk {
+// Loaded source chunk of a token.
+struct Raw {
   u32x4 a, b;
-  float scale;
+  float scale;   // this lane's block scale
+  u32x4 sc4;     // lanes 0 and 32 of a wave: the scales of their 4 blocks
 };
 
+// Lanes 0 and 32 of each wave collect the scales of the 4 blocks their
+// half-wave covers (lanes +0, +8, +16, +24), so that each half-wave writes
+// its 16 bytes of scales with one store.
+__device__ __forceinline__ void gather_scales(Raw& r) {
+  const int base = threadIdx.x & 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    r.sc4[q] = __float_as_uint(__shfl(r.scale, base + 8 * q, 64));
+}
+
 template <int IN>  // 0: BF16 in -> FP8, 1: BF16 in -> BF16, 2: FP8 in -> FP8
-__device__ __forceinline__ Chunk make_chunk(const DispatchArgs& p, int64_t i, int c, bool active) {
-  Chunk ch;
-  ch.scale = 0.0f;
+__device__ __forceinline__ Raw load_chunk(const DispatchArgs& p, int64_t i, int c, bool active) {
+  Raw r;
+  const u32x4 zero{0, 0, 0, 0};
+  r.scale = 0.0f;
   if constexpr (IN == 2) {
     const uint8_t* src = static_cast<const uint8_t*>(p.x) + i * p.ld_x;
-    ch.a = active ? *reinterpret_cast<const u32x4*>(src + 16 * c) : u32x4{0, 0, 0, 0};
-    ch.b = ch.a;
-    ch.scale = active ? p.x_scales[i * p.ld_s + (c >> 3)] : 0.0f;
-    return ch;
+    r.a = active ? *reinterpret_cast<const u32x4*>(src + 16 * c) : zero;
+    r.b = zero;
+    r.scale = active ? p.x_scales[i * p.ld_s + (c >> 3)] : 0.0f;
   } else {
     const uint16_t* src = static_cast<const uint16_t*>(p.x) + i * p.ld_x;
     const u32x4* s4 = reinterpret_cast<const u32x4*>(src + 16 * c);
-    const u32x4 zero{0, 0, 0, 0};
-    ch.a = active ? s4[0] : zero;
-    ch.b = active ? s4[1] : zero;
-    if constexpr (IN == 1) return ch;
-    float f[16];
+    r.a = active ? s4[0] : zero;
+    r.b = active ? s4[1] : zero;
+  }
+  return r;
+}
+
+// Quantise a loaded BF16 chunk: 16 codes in r.a, block scale in r.scale.
+__device__ __forceinline__ void quantize(Raw& r) {
+  float f[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f[2 * q] = bf16_lo(r.a[q]);
+    f[2 * q + 1] = bf16_hi(r.a[q]);
+    f[8 + 2 * q] = bf16_lo(r.b[q]);
+    f[8 + 2 * q + 1] = bf16_hi(r.b[q]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(f[q]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+  u32x4 out{0, 0, 0, 0};
+  r.scale = 0.0f;
+  if (amax != 0.0f) {
+    const float scale = amax / 448.0f;
+    r.scale = scale;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      f[2 * q] = bf16_lo(ch.a[q]);
-      f[2 * q + 1] = bf16_hi(ch.a[q]);
-      f[8 + 2 * q] = bf16_lo(ch.b[q]);
-      f[8 + 2 * q + 1] = bf16_hi(ch.b[q]);
+      uint32_t w = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) w |= to_e4m3(f[4 * q + b] / scale) << (8 * b);
+      out[q] = w;
     }
-    float amax = 0.0f;
-#pragma unroll
-    for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(f[q]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
-    u32x4 out{0, 0, 0, 0};
-    if (amax != 0.0f) {
-      const float scale = amax / 448.0f;
-      ch.scale = scale;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) w |= to_e4m3(f[4 * q + b] / scale) << (8 * b);
-        out[q] = w;
-      }
-    }
-    ch.a = out;
-    return ch;
   }
+  r.a = out;
 }
 
+// Stores this lane's part of a row: 16 bytes of codes (or 32 of bf16), and
+// the scales -- 16 bytes per half-wave when its 4 blocks all exist, else one
+// 4-byte store per block.
 template <int IN>
-__device__ __forceinline__ void put_row(const DispatchArgs& p, const Chunk& ch, uint8_t* row, int c) {
+__device__ __forceinline__ void put_row(const DispatchArgs& p, const Raw& r, uint8_t* row, int c, int C) {
   if constexpr (IN == 1) {
-    store_nt(ch.a, row + 32 * c);
-    store_nt(ch.b, row + 32 * c + 16);
+    store_nt(r.a, row + 32 * c);
+    store_nt(r.b, row + 32 * c + 16);
   } else {
-    store_nt(ch.a, row + 16 * c);
-    if ((c & 7) == 0)
-      __builtin_nontemporal_store(ch.scale, reinterpret_cast<float*>(row + p.H + 4 * (c >> 3)));
+    if (c < C) store_nt(r.a, row + 16 * c);
+    const int hb = (c >> 5) << 2;                 // first block of the half-wave
+    if (hb + 4 <= (C >> 3)) {
+      if ((c & 31) == 0) store_nt(r.sc4, row + p.H + 4 * hb);
+    } else if ((c & 7) == 0 && c < C) {
+      __builtin_nontemporal_store(r.scale, reinterpret_cast<float*>(row + p.H + 4 * (c >> 3)));
+    }
   }
 }
 
-template <int IN, bool HT>
+// Validity of the K entries of one token row: in range and not a repeat.
+template <int KMAX>
+__device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool present, int (&e)[KMAX],
+                                        bool (&ok)[KMAX]) {
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) e[k] = (present && k < K) ? row[k] : -1;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    bool dup = false;
+#pragma unroll
+    for (int j = 0; j < k; ++j) dup |= e[j] == e[k];
+    ok[k] = present && k < K && e[k] >= 0 && e[k] < E && !dup;
+  }
+}
+
+template <int IN, bool HT, bool PAYLOAD, int KMAX>
 __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs p) {
+  __shared__ int s_rank[KMAX + kMaxNodes];
   const int c = threadIdx.x;
   const int C = p.H / 16;
-  const bool active = c < C;
+  const bool active = PAYLOAD && c < C;
+  const int K = p.K, E = p.E, N = p.N;
   for (int64_t i = blockIdx.x; i < p.n; i += gridDim.x) {
-    const Chunk ch = make_chunk<IN>(p, i, c, active);
-    const int32_t t = static_cast<int32_t>(i % p.T);
-    const int32_t s = static_cast<int32_t>(i / p.T);
-    if constexpr (HT) {
-      for (int n = 0; n < p.N; ++n) {
-        const int32_t r = p.node_row[i * p.N + n];
-        if (r < 0) continue;
-        if (active) put_row<IN>(p, ch, p.st1 + static_cast<int64_t>(r) * p.row_bytes, c);
-        if (c == 0) {
-          p.m1_tok[r] = t;
-          p.m1_src[r] = s;
-        }
-        for (int k = c; k < p.K; k += blockDim.x) {
-          p.m1_topk[static_cast<int64_t>(r) * p.K + k] = p.topk[i * p.K + k];
-          if (p.w) p.m1_w[static_cast<int64_t>(r) * p.K + k] = p.w[i * p.K + k];
-        }
+    Raw raw;
+    if constexpr (PAYLOAD) raw = load_chunk<IN>(p, i, c, active);
+    const int s = static_cast<int>(i / p.T);
+    const int t = static_cast<int>(i - static_cast<int64_t>(s) * p.T);
+    const int tt = t / kTile;
+    const int j = s * p.tps + tt;          // tile of this token
+    const int nb = t - tt * kTile;         // earlier tokens in the tile
+
+    // This token's entries (uniform).
+    int me[KMAX];
+    bool mok[KMAX];
+    entries<KMAX>(p.topk + i * K, K, E, true, me, mok);
+    uint64_t my_nodes = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (mok[k]) my_nodes |= 1ull << (me[k] / p.P);
+
+    // In-tile ranks by one ballot per entry / node (wave 0).
+    if (threadIdx.x < 64) {
+      const int l = threadIdx.x;
+      const bool present = l < nb;
+      int oe[KMAX];
+      bool ook[KMAX];
+      entries<KMAX>(p.topk + (i - nb + (present ? l : 0)) * K, K, E, present, oe, ook);
+      uint64_t o_nodes = 0;
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (ook[k]) o_nodes |= 1ull << (oe[k] / p.P);
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        if (k >= K) continue;
+        bool has = false;
+#pragma unroll
+        for (int q = 0; q < KMAX; ++q) has |= ook[q] && oe[q] == me[k];
+        const int r = __popcll(__ballot(has));
+        if (l == 0) s_rank[k] = r;
       }
-      for (int k = 0; k < p.K; ++k) {
-        const int32_t r = p.row2[i * p.K + k];
-        if (r < 0) continue;
-        if (active) put_row<IN>(p, ch, p.st2 + static_cast<int64_t>(r) * p.row_bytes, c);
-        if (c == 0) {
-          p.m2_src[r] = s;
-          p.m2_tok[r] = t;
-          p.m2_k[r] = k;
-        }
-      }
-    } else {
-      for (int k = 0; k < p.K; ++k) {
-        const int32_t slot = p.slot_map[i * p.K + k];
-        if (slot < 0) continue;
-        uint8_t* msg = p.ll_buf + static_cast<int64_t>(slot) * p.msg_bytes;
-        if (active) put_row<IN>(p, ch, msg, c);
-        if (c == 0) {
-          const i32x4 hdr{t, s, k, 0};
-          __builtin_nontemporal_store(hdr, reinterpret_cast<i32x4*>(msg + p.row_bytes));
+      if (HT) {
+        for (int n = 0; n < N; ++n) {
+          if (!((my_nodes >> n) & 1)) continue;
+          const int r = __popcll(__ballot((o_nodes >> n) & 1));
+          if (l == 0) s_rank[KMAX + n] = r;
         }
       }
     }
+    __syncthreads();
+
+    // Positions (uniform), written to the handle's maps.
+    int pos[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      pos[k] = -1;
+      if (mok[k]) {
+        const int pre = p.hist_e[static_cast<int64_t>(j) * E + me[k]] + s_rank[k];
+        pos[k] = HT ? pre : (me[k] * p.S + s) * p.slots + pre;
+      }
+    }
+    if (c < K) {
+      int v = -1;
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (k == c) v = pos[k];
+      (HT ? p.row2 : p.slot_map)[i * K + c] = v;
+    }
+    // Stage-1 row of destination node n (uniform), or -1.
+    auto node_pos = [&](int n) -> int {
+      return ((my_nodes >> n) & 1) ? p.hist_n[static_cast<int64_t>(j) * N + n] + s_rank[KMAX + n] : -1;
+    };
+    if constexpr (HT) {
+      for (int n = c; n < N; n += blockDim.x) p.node_row[i * N + n] = node_pos(n);
+    }
+
+    if constexpr (PAYLOAD) {
+      if constexpr (IN == 0) quantize(raw);
+      if constexpr (IN != 1) gather_scales(raw);
+      if constexpr (HT) {
+        for (int n = 0; n < N; ++n) {
+          if (!((my_nodes >> n) & 1)) continue;
+          const int32_t r = node_pos(n);
+          if (IN != 1 || active) put_row<IN>(p, raw, p.st1 + static_cast<int64_t>(r) * p.row_bytes, c, C);
+          if (c == 0) {
+            p.m1_tok[r] = t;
+            p.m1_src[r] = s;
+          }
+          for (int k = c; k < K; k += blockDim.x) {
+            int ev = -1;
+#pragma unroll
+            for (int q = 0; q < KMAX; ++q)
+              if (q == k) ev = me[q];
+            p.m1_topk[static_cast<int64_t>(r) * K + k] = ev;
+            if (p.w) p.m1_w[static_cast<int64_t>(r) * K + k] = p.w[i * K + k];
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int32_t r = pos[k];
+          if (r < 0) continue;
+          if (IN != 1 || active) put_row<IN>(p, raw, p.st2 + static_cast<int64_t>(r) * p.row_bytes, c, C);
+          if (c == 0) {
+            p.m2_src[r] = s;
+            p.m2_tok[r] = t;
+            p.m2_k[r] = k;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int32_t slot = pos[k];
+          if (slot < 0) continue;
+          uint8_t* msg = p.ll_buf + static_cast<int64_t>(slot) * p.msg_bytes;
+          if (IN != 1 || active) put_row<IN>(p, raw, msg, c, C);
+          if (c == 0) {
+            const i32x4 hdr{t, s, k, 0};
+            __builtin_nontemporal_store(hdr, reinterpret_cast<i32x4*>(msg + p.row_bytes));
+          }
+        }
+      }
+    }
+    __syncthreads();   // s_rank is reused by the next token of this workgroup
   }
 }
 
-template <int IN>
-hipError_t launch_in(const DispatchArgs& p, dim3 grid, dim3 block, hipStream_t stream) {
-  if (p.ht) dispatch_kernel<IN, true><<<grid, block, 0, stream>>>(p);
-  else dispatch_kernel<IN, false><<<grid, block, 0, stream>>>(p);
-  return hipGetLastError();
+template <int IN, bool PAYLOAD, int KMAX>
+void launch_k(const DispatchArgs& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.ht) dispatch_kernel<IN, true, PAYLOAD, KMAX><<<grid, block, 0, stream>>>(p);
+  else dispatch_kernel<IN, false, PAYLOAD, KMAX><<<grid, block, 0, stream>>>(p);
+}
+
+template <int IN, bool PAYLOAD>
+void launch_in(const DispatchArgs& p, dim3 grid, dim3 block, hipStream_t stream) {
+  if (p.K <= 8) launch_k<IN, PAYLOAD, 8>(p, grid, block, stream);
+  else launch_k<IN, PAYLOAD, 32>(p, grid, block, stream);
 }
 
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs& p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;
-  const int C = p.H / 16;
-  const int threads = ((C + 63) / 64) * 64;
   int64_t blocks = p.n;
   if (p.max_blocks > 0 && blocks > p.max_blocks) blocks = p.max_blocks;
   if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
-  if (p.in_fp8) return launch_in<2>(p, grid, block, stream);
-  if (p.out_fp8) return launch_in<0>(p, grid, block, stream);
-  return launch_in<1>(p, grid, block, stream);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (!p.payload) {
+    // Maps only: one wave per token.
+    launch_in<0, false>(p, grid, dim3(64), stream);
+    return hipGetLastError();
+  }
+  const int C = p.H / 16;
+  const dim3 block(((C + 63) / 64) * 64);
+  if (p.in_fp8) launch_in<2, true>(p, grid, block, stream);
+  else if (p.out_fp8) launch_in<0, true>(p, grid, block, stream);
+  else launch_in<1, true>(p, grid, block, stream);
+  return hipGetLastError();
 }
 
 }  // namespace ep

@@ -8,7 +8,7 @@
 #include <cstdint>
 #include <vector>
 
-#include "../../include/ep.h"
+#include "ep.h"
 
 #define EP_API extern "C" __attribute__((visibility("default")))
 
@@ -20,7 +20,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxNodes = 64;
 constexpr int kMaxRanks = 1024;
 constexpr int kMaxHidden = 16384;
-constexpr int kLayoutTile = 256;   // tokens per layout workgroup
+constexpr int kLayoutTile = 64;    // tokens per layout tile (one wave)
 
 constexpr uint32_t kGroupMagic = 0x45504752u;   // "EPGR"
 constexpr uint32_t kHandleMagic = 0x4550484Eu;  // "EPHN"
@@ -77,6 +77,8 @@ struct Handle {
   int tps = 0;     // layout tiles per source
   int n_tiles = 0;
   hipStream_t stream = nullptr;
+  bool maps_ready = false;       // slot/row maps written (by dispatch)
+  int32_t* done = nullptr;       // last-workgroup counter of the count kernel
   int32_t* topk = nullptr;       // copy of topk_idx [n_max, K]
   int32_t* slot_map = nullptr;   // LL [n_max, K]
   int32_t* ll_count = nullptr;   // LL [E, S]
@@ -86,7 +88,7 @@ struct Handle {
   int32_t* off1 = nullptr;       // HT [R]
   int32_t* c2 = nullptr;         // HT [E]
   int32_t* off2 = nullptr;       // HT [E]
-  int32_t* hist_e = nullptr;     // [tiles_max, E]
+  int32_t* hist_e = nullptr;     // [tiles_max, E] tile counts -> prefixes
   int32_t* hist_n = nullptr;     // [tiles_max, N]
 };
 
@@ -123,6 +125,7 @@ struct LayoutArgs {
   int32_t* c2;
   int32_t* off2;
   int32_t* err;
+  int32_t* done;
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 
@@ -138,18 +141,21 @@ struct DispatchArgs {
   int in_fp8;             // tokens arrive quantised
   int out_fp8;            // payload is FP8
   int64_t n;
-  int T, K, N, H;
+  int T, K, N, H, E, S, P, slots, tps;
   int64_t row_bytes, msg_bytes;
   int ht;
+  int payload;            // 0 = compute the maps only
   int max_blocks;         // 0 = one workgroup per token
+  const int32_t* topk;    // the handle's copy [n, K]
+  const int32_t* hist_e;  // tile prefixes [tiles, E]
+  const int32_t* hist_n;  // [tiles, N]
+  int32_t* slot_map;      // LL out [n, K]
+  int32_t* row2;          // HT out [n, K]
+  int32_t* node_row;      // HT out [n, N]
   // LL
-  const int32_t* slot_map;
   uint8_t* ll_buf;
   // HT
-  const int32_t* topk;
   const float* w;
-  const int32_t* node_row;
-  const int32_t* row2;
   uint8_t* st1;
   int32_t* m1_tok;
   int32_t* m1_src;

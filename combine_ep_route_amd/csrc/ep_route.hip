@@ -118,10 +118,169 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   if (active && lane < a.K) a.topk[t * a.K + lane] = mine;
 }
 
+// ---------------------------------------------------------------------------
+// Fast path: 32 lanes per token (two tokens per wave), V = E/32 consecutive
+// experts per lane (one or more 16-byte loads), a node spans LPN = P/V lanes
+// (a power of two).  All cross-lane steps are DPP row permutations or
+// ds_swizzle inside the 32-lane half, so nothing waits on LDS except the
+// single exchange of the N node scores.
+// ---------------------------------------------------------------------------
+
+constexpr int kFastTokensPerBlock = 8;   // 4 waves x 2 tokens
+
+template <int CTRL>
+__device__ __forceinline__ int dpp(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int swz_xor16(int x) {
+  return __builtin_amdgcn_ds_swizzle(x, 0x401F);   // xor lane 16 within 32
+}
+constexpr int kQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kHalfMirror = 0x141;   // lane i <-> 7-i inside 8
+constexpr int kRowMirror = 0x140;    // lane i <-> 15-i inside 16
+
+template <int STEP>
+__device__ __forceinline__ int xchg(int x) {
+  if constexpr (STEP == 0) return dpp<kQuadXor1>(x);
+  else if constexpr (STEP == 1) return dpp<kQuadXor2>(x);
+  else if constexpr (STEP == 2) return dpp<kHalfMirror>(x);
+  else if constexpr (STEP == 3) return dpp<kRowMirror>(x);
+  else return swz_xor16(x);
+}
+template <int STEP>
+__device__ __forceinline__ float xchgf(float x) { return __int_as_float(xchg<STEP>(__float_as_int(x))); }
+
+// (v, i) beats (w, j) when v > w, or v == w and i < j.
+__device__ __forceinline__ bool beats(float v, int i, float w, int j) {
+  return v > w || (v == w && i < j);
+}
+
+template <int STEP>
+__device__ __forceinline__ void argmax_step(float& v, int& i) {
+  const float ov = xchgf<STEP>(v);
+  const int oi = xchg<STEP>(i);
+  if (beats(ov, oi, v, i)) { v = ov; i = oi; }
+}
+
+// Merge the node top-2 (a1 >= a2) with a partner group's over one exchange.
+template <int STEP>
+__device__ __forceinline__ void top2_step(float& a1, float& a2) {
+  const float b1 = xchgf<STEP>(a1), b2 = xchgf<STEP>(a2);
+  const float hi = fmaxf(a1, b1), lo = fminf(a1, b1);
+  a2 = fmaxf(lo, fmaxf(a2, b2));
+  a1 = hi;
+}
+
+// Steps that cover a group of LPN lanes with disjoint partial sets at every
+// step: (xor 16), row mirror, half mirror, quad xor 2, quad xor 1.
+template <int LPN>
+__device__ __forceinline__ void node_top2(float& a1, float& a2) {
+  if constexpr (LPN >= 32) top2_step<4>(a1, a2);
+  if constexpr (LPN >= 16) top2_step<3>(a1, a2);
+  if constexpr (LPN >= 8) top2_step<2>(a1, a2);
+  if constexpr (LPN >= 4) top2_step<1>(a1, a2);
+  if constexpr (LPN >= 2) top2_step<0>(a1, a2);
+}
+
+template <int V, int LPN>
+__global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
+  __shared__ float s_node[kFastTokensPerBlock][32];
+  const int half = threadIdx.x >> 5;         // token slot in the block
+  const int hl = threadIdx.x & 31;           // lane inside the token's 32
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kFastTokensPerBlock + half;
+  const bool active = t < a.n;
+  const float* row = a.scores + (active ? t : 0) * a.ld + hl * V;
+
+  float val[V];
+#pragma unroll
+  for (int q = 0; q < V / 4; ++q) {
+    const float4 f = active ? reinterpret_cast<const float4*>(row)[q] : make_float4(0.f, 0.f, 0.f, 0.f);
+    val[4 * q] = f.x; val[4 * q + 1] = f.y; val[4 * q + 2] = f.z; val[4 * q + 3] = f.w;
+  }
+  const int N = a.N;
+  const int node = hl / LPN;
+  bool keep = true;
+  if (a.M > 0) {
+    // top-2 (or top-1) of the lane's V scores, merged across the node's lanes
+    float a1 = val[0], a2 = -INFINITY;
+#pragma unroll
+    for (int v = 1; v < V; ++v) {
+      const float x = val[v];
+      a2 = fmaxf(a2, fminf(a1, x));
+      a1 = fmaxf(a1, x);
+    }
+    node_top2<LPN>(a1, a2);
+    const float ns = a.J == 2 ? a1 + a2 : a1;
+    if (hl % LPN == 0) s_node[half][node] = ns;
+    __syncthreads();
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      const float o = s_node[half][m];
+      rank += (o > ns) || (o == ns && m < node);
+    }
+    keep = rank < a.M;
+  }
+
+  // K rounds of a 32-lane arg-max over the remaining candidates.
+  const int e0 = hl * V;
+  bool alive[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) alive[v] = keep;
+  int mine = -1;
+  for (int k = 0; k < a.K; ++k) {
+    float bv = -INFINITY;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (alive[v] && beats(val[v], e0 + v, bv, bi)) { bv = val[v]; bi = e0 + v; }
+    argmax_step<0>(bv, bi);
+    argmax_step<1>(bv, bi);
+    argmax_step<2>(bv, bi);
+    argmax_step<3>(bv, bi);
+    argmax_step<4>(bv, bi);
+    if (hl == k) mine = bi;
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (bi == e0 + v) alive[v] = false;
+  }
+  if (active && hl < a.K) a.topk[t * a.K + hl] = mine;
+}
+
+template <int V>
+hipError_t launch_fast_v(const RouteArgs& a, int lpn, dim3 grid, dim3 block, hipStream_t stream) {
+  switch (lpn) {
+    case 1: route_fast_kernel<V, 1><<<grid, block, 0, stream>>>(a); break;
+    case 2: route_fast_kernel<V, 2><<<grid, block, 0, stream>>>(a); break;
+    case 4: route_fast_kernel<V, 4><<<grid, block, 0, stream>>>(a); break;
+    case 8: route_fast_kernel<V, 8><<<grid, block, 0, stream>>>(a); break;
+    case 16: route_fast_kernel<V, 16><<<grid, block, 0, stream>>>(a); break;
+    default: route_fast_kernel<V, 32><<<grid, block, 0, stream>>>(a); break;
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
+  // Fast path: E a multiple of 128 up to 512, K <= 32, a node spanning a
+  // power-of-two number of lanes, node sums of at most 2 scores, 16-byte
+  // aligned rows.
+  const int P = a.E / a.N;
+  const int V = a.E / 32;
+  const bool aligned = (reinterpret_cast<uintptr_t>(a.scores) % 16 == 0) && (a.ld % 4 == 0);
+  if (aligned && a.E % 128 == 0 && V <= 16 && a.K <= 32 && a.J <= 2 && P % V == 0) {
+    const int lpn = P / V;
+    if ((lpn & (lpn - 1)) == 0 && lpn <= 32) {
+      const int64_t blocks = (a.n + kFastTokensPerBlock - 1) / kFastTokensPerBlock;
+      const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+      if (V == 4) return launch_fast_v<4>(a, lpn, grid, block, stream);
+      if (V == 8) return launch_fast_v<8>(a, lpn, grid, block, stream);
+      if (V == 12) return launch_fast_v<12>(a, lpn, grid, block, stream);
+      if (V == 16) return launch_fast_v<16>(a, lpn, grid, block, stream);
+    }
+  }
   const int64_t blocks = (a.n + kTokensPerBlock - 1) / kTokensPerBlock;
   const dim3 grid(static_cast<unsigned>(blocks)), block(256);
   const int nv = (a.E + 63) / 64;

@@ -132,6 +132,7 @@ ep_status_t ensure_device(Group* g, hipStream_t stream) {
   EP_HIP(hipGetDevice(&g->device));
   EP_HIP(hipDeviceGetAttribute(&g->num_cu, hipDeviceAttributeMultiprocessorCount, g->device));
   EP_HIP(launch_fill_i32(g->err, 1, 0, stream));
+  for (Handle* h : g->handles) EP_HIP(launch_fill_i32(h->done, 1, 0, stream));
   g->dev_ready = true;
   return EP_OK;
 }
@@ -157,6 +158,45 @@ void fill_view(ep_tensor_t* v, void* data, int32_t dtype, int64_t d0, int64_t d1
 int dispatch_block_cap(const Group* g) {
   // One workgroup per token by default; with a CU cap, 4 per allowed CU.
   return g->cfg.num_cus > 0 ? g->cfg.num_cus * 4 : 0;
+}
+
+// The handle-dependent part of a dispatch launch.
+DispatchArgs dispatch_base(const Handle* h) {
+  const Group* g = h->g;
+  DispatchArgs p{};
+  p.n = h->n;
+  p.T = h->T;
+  p.K = g->cfg.top_k;
+  p.N = g->cfg.num_nodes;
+  p.H = g->cfg.hidden;
+  p.E = g->cfg.num_experts;
+  p.S = g->cfg.num_src_ranks;
+  p.P = g->P;
+  p.slots = g->cfg.max_tokens_per_rank;
+  p.tps = h->tps;
+  p.row_bytes = g->row_bytes;
+  p.msg_bytes = g->msg_bytes;
+  p.ht = g->cfg.mode == EP_MODE_HT;
+  p.max_blocks = dispatch_block_cap(g);
+  p.topk = h->topk;
+  p.hist_e = h->hist_e;
+  p.hist_n = h->hist_n;
+  p.slot_map = h->slot_map;
+  p.row2 = h->row2;
+  p.node_row = h->node_row;
+  return p;
+}
+
+// Make sure the slot / row maps exist (dispatch writes them; without a
+// dispatch, a maps-only pass computes them).
+ep_status_t ensure_maps(Handle* h, hipStream_t stream) {
+  if (h->maps_ready) return EP_OK;
+  DispatchArgs p = dispatch_base(h);
+  p.payload = 0;
+  p.max_blocks = 0;
+  const ep_status_t st = from_hip(launch_dispatch(p, stream));
+  if (st == EP_OK) h->maps_ready = true;
+  return st;
 }
 
 }  // namespace
@@ -251,7 +291,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   for (int hs = 0; st == EP_OK && hs < cfg.max_handles; ++hs) {
     const size_t nm = static_cast<size_t>(g->n_max);
     const size_t tiles = static_cast<size_t>(g->tiles_max);
-    size_t bytes = align_up(nm * K * 4);                       // topk copy
+    size_t bytes = align_up(nm * K * 4) + align_up(4);         // topk copy, counter
     if (cfg.mode == EP_MODE_LL) {
       bytes += align_up(nm * K * 4) + align_up(static_cast<size_t>(E) * S * 4);
     } else {
@@ -266,6 +306,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
     h->in_use = false;
     Carve cv{b};
     h->topk = cv.take<int32_t>(nm * K);
+    h->done = cv.take<int32_t>(1);
     if (cfg.mode == EP_MODE_LL) {
       h->slot_map = cv.take<int32_t>(nm * K);
       h->ll_count = cv.take<int32_t>(static_cast<size_t>(E) * S);
@@ -411,6 +452,8 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.c2 = h->c2;
   a.off2 = h->off2;
   a.err = g->err;
+  a.done = h->done;
+  h->maps_ready = (n == 0);
   if (n == 0 && a.ht) {
     // Nothing routed: counts and offsets are zero.
     EP_HIP(launch_fill_i32(h->c1, g->R, 0, s));
@@ -462,6 +505,9 @@ EP_API ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tenso
   Group* g = h->g;
   const bool ll = g->cfg.mode == EP_MODE_LL;
   const int E = g->cfg.num_experts, K = g->cfg.top_k, N = g->cfg.num_nodes, S = g->cfg.num_src_ranks;
+  if (which == EP_MAP_LL_SLOT || which == EP_MAP_HT_NODE_ROW || which == EP_MAP_HT_ROW) {
+    if (const ep_status_t st = ensure_maps(h, h->stream); st != EP_OK) return st;
+  }
   switch (which) {
     case EP_MAP_LL_SLOT: if (!ll) break; fill_view(view, h->slot_map, EP_DTYPE_I32, h->n, K, EP_TAG_NONE); return EP_OK;
     case EP_MAP_LL_COUNT: if (!ll) break; fill_view(view, h->ll_count, EP_DTYPE_I32, E, S, EP_TAG_RECV_EXPERT_COUNTER_DEVICE); return EP_OK;
@@ -512,7 +558,8 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
   h->stream = s;
 
-  DispatchArgs p{};
+  DispatchArgs p = dispatch_base(h);
+  p.payload = 1;
   p.x = tokens->data;
   p.ld_x = tokens->strides[0];
   p.in_fp8 = in_fp8;
@@ -521,20 +568,7 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
     p.ld_s = scales->strides[0];
   }
   p.out_fp8 = g->fp8;
-  p.n = h->n;
-  p.T = h->T;
-  p.K = K;
-  p.N = g->cfg.num_nodes;
-  p.H = H;
-  p.row_bytes = g->row_bytes;
-  p.msg_bytes = g->msg_bytes;
-  p.ht = !ll;
-  p.max_blocks = dispatch_block_cap(g);
-  p.slot_map = h->slot_map;
   p.ll_buf = g->ll_buf;
-  p.topk = h->topk;
-  p.node_row = h->node_row;
-  p.row2 = h->row2;
   p.w = topk_weights ? static_cast<const float*>(topk_weights->data) : nullptr;
   p.st1 = g->st1;
   p.m1_tok = g->m1_tok;
@@ -546,6 +580,7 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   p.m2_tok = g->m2_tok;
   p.m2_k = g->m2_k;
   if (const ep_status_t st = from_hip(launch_dispatch(p, s)); st != EP_OK) return st;
+  h->maps_ready = true;
   if (recv_counts) {
     const size_t bytes = (ll ? static_cast<size_t>(E) * S : static_cast<size_t>(E)) * sizeof(int32_t);
     EP_HIP(hipMemcpyAsync(recv_counts->data, ll ? h->ll_count : h->c2, bytes, hipMemcpyDeviceToDevice, s));
@@ -608,6 +643,7 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
   const hipStream_t s = as_stream(stream);
   if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
   h->stream = s;
+  if (const ep_status_t st = ensure_maps(h, s); st != EP_OK) return st;
   CombineArgs a{};
   a.y = static_cast<const uint16_t*>(y2.data);
   a.ld_y = y2.strides[0];
