@@ -10,21 +10,22 @@
 // notes" -- quantisation inside the send kernel's prepare stage, message
 // sizes 7408 B (FP8) / 14352 B (BF16).
 //
-// Mapping: one workgroup per token (grid-stride when a CU cap is set).
-//  1. Thread c issues the loads of elements [16c, 16c+16) (two 16-byte
-//     loads of bf16) first, so they are in flight during step 2.
-//  2. Wave 0 ranks the token inside its 64-token tile: lane l looks at the
-//     l-th earlier token of the tile, and one ballot per expert (and per
-//     destination node) counts the earlier tokens that share it.  Adding the
-//     tile's prefix from the handle gives the slot / row of every entry; the
-//     positions are workgroup-uniform and kept in scalar registers.
+// Mapping: a token is split over W waves, each owning a contiguous range of
+// 64*NV 16-element chunks (lane l: chunks c0 + v*64, v < NV); four waves per
+// 256-thread workgroup and no barriers -- each wave ranks its token itself.
+//  1. The token's payload loads are issued first (16-byte loads).
+//  2. Its rank inside its 64-token tile: lane l looks at the l-th earlier
+//     token of the tile and one ballot per entry (and per destination node)
+//     counts the earlier tokens sharing it; adding the tile prefix from the
+//     handle gives every slot / row.  Positions are wave-uniform.
 //  3. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 and q = E4M3(x/scale),
 //     both IEEE fp32 divisions (round to nearest even).
-//  4. The 16-byte chunk of codes is stored to every destination row with
-//     non-temporal stores (nothing on this GPU reads the rows back during
-//     the pass); each half-wave writes its 4 block scales with one 16-byte
-//     store.
+//  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
+//     size rounded up to 128 B; the padding is never written).  Each chunk
+//     of codes goes to every destination row with non-temporal stores
+//     (nothing on this GPU reads the rows back during the pass); each
+//     half-wave writes its 4 block scales with one 16-byte store.
 #include "ep_internal.h"
 
 namespace ep {
@@ -65,18 +66,8 @@ __device__ __forceinline__ void store_nt(u32x4 v, uint8_t* p) {
 struct Raw {
   u32x4 a, b;
   float scale;   // this lane's block scale
-  u32x4 sc4;     // lanes 0 and 32 of a wave: the scales of their 4 blocks
+  u32x4 sc4;     // lanes 0 and 32: the scales of their half-wave's 4 blocks
 };
-
-// Lanes 0 and 32 of each wave collect the scales of the 4 blocks their
-// half-wave covers (lanes +0, +8, +16, +24), so that each half-wave writes
-// its 16 bytes of scales with one store.
-__device__ __forceinline__ void gather_scales(Raw& r) {
-  const int base = threadIdx.x & 32;
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    r.sc4[q] = __float_as_uint(__shfl(r.scale, base + 8 * q, 64));
-}
 
 template <int IN>  // 0: BF16 in -> FP8, 1: BF16 in -> BF16, 2: FP8 in -> FP8
 __device__ __forceinline__ Raw load_chunk(const DispatchArgs& p, int64_t i, int c, bool active) {
@@ -129,14 +120,24 @@ __device__ __forceinline__ void quantize(Raw& r) {
   r.a = out;
 }
 
-// Stores this lane's part of a row: 16 bytes of codes (or 32 of bf16), and
-// the scales -- 16 bytes per half-wave when its 4 blocks all exist, else one
+// Lanes 0 and 32 collect the scales of the 4 blocks their half-wave covers
+// (lanes +0, +8, +16, +24), so each half-wave writes them with one store.
+__device__ __forceinline__ void gather_scales(Raw& r, int lane) {
+  const int base = lane & 32;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) r.sc4[q] = __float_as_uint(__shfl(r.scale, base + 8 * q, 64));
+}
+
+// Stores chunk c of a row: 16 bytes of codes (or 32 of bf16), and the
+// scales -- 16 bytes per half-wave when its 4 blocks all exist, else one
 // 4-byte store per block.
 template <int IN>
-__device__ __forceinline__ void put_row(const DispatchArgs& p, const Raw& r, uint8_t* row, int c, int C) {
+__device__ __forceinline__ void put_chunk(const DispatchArgs& p, const Raw& r, uint8_t* row, int c, int C) {
   if constexpr (IN == 1) {
-    store_nt(r.a, row + 32 * c);
-    store_nt(r.b, row + 32 * c + 16);
+    if (c < C) {
+      store_nt(r.a, row + 32 * c);
+      store_nt(r.b, row + 32 * c + 16);
+    }
   } else {
     if (c < C) store_nt(r.a, row + 16 * c);
     const int hb = (c >> 5) << 2;                 // first block of the half-wave
@@ -163,23 +164,34 @@ __device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool p
   }
 }
 
-template <int IN, bool HT, bool PAYLOAD, int KMAX>
-__global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs p) {
-  __shared__ int s_rank[KMAX + kMaxNodes];
-  const int c = threadIdx.x;
+// One wave per token, four tokens per 256-thread workgroup; lane owns chunks
+// c = v*64 + lane, v < NV (16 elements each).  No barriers: everything
+// shared inside a token is a wave-uniform ballot result.
+template <int IN, bool HT, bool PAYLOAD, int KMAX, int NV>
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
+  const int lane = threadIdx.x & 63;
   const int C = p.H / 16;
-  const bool active = PAYLOAD && c < C;
   const int K = p.K, E = p.E, N = p.N;
-  for (int64_t i = blockIdx.x; i < p.n; i += gridDim.x) {
-    Raw raw;
-    if constexpr (PAYLOAD) raw = load_chunk<IN>(p, i, c, active);
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t total = p.n * W;
+  for (int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); gw < total; gw += waves) {
+    const int64_t i = gw / W;                       // token
+    const int part = static_cast<int>(gw - i * W);  // which chunk range of it
+    const int c0 = part * NV * 64 + lane;           // this lane's first chunk
+    // 1. Payload loads first, so they are in flight during the ranking.
+    Raw raw[NV];
+    if constexpr (PAYLOAD) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) raw[v] = load_chunk<IN>(p, i, c0 + v * 64, c0 + v * 64 < C);
+    }
     const int s = static_cast<int>(i / p.T);
     const int t = static_cast<int>(i - static_cast<int64_t>(s) * p.T);
     const int tt = t / kTile;
     const int j = s * p.tps + tt;          // tile of this token
     const int nb = t - tt * kTile;         // earlier tokens in the tile
 
-    // This token's entries (uniform).
+    // 2. This token's entries (uniform) and its rank inside the tile: lane l
+    //    holds the l-th earlier token of the tile; one ballot per entry/node.
     int me[KMAX];
     bool mok[KMAX];
     entries<KMAX>(p.topk + i * K, K, E, true, me, mok);
@@ -187,89 +199,88 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs p) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if (mok[k]) my_nodes |= 1ull << (me[k] / p.P);
+    const bool present = lane < nb;
+    int oe[KMAX];
+    bool ook[KMAX];
+    entries<KMAX>(p.topk + (i - nb + (present ? lane : 0)) * K, K, E, present, oe, ook);
+    uint64_t o_nodes = 0;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (ook[k]) o_nodes |= 1ull << (oe[k] / p.P);
 
-    // In-tile ranks by one ballot per entry / node (wave 0).
-    if (threadIdx.x < 64) {
-      const int l = threadIdx.x;
-      const bool present = l < nb;
-      int oe[KMAX];
-      bool ook[KMAX];
-      entries<KMAX>(p.topk + (i - nb + (present ? l : 0)) * K, K, E, present, oe, ook);
-      uint64_t o_nodes = 0;
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k)
-        if (ook[k]) o_nodes |= 1ull << (oe[k] / p.P);
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        if (k >= K) continue;
-        bool has = false;
-#pragma unroll
-        for (int q = 0; q < KMAX; ++q) has |= ook[q] && oe[q] == me[k];
-        const int r = __popcll(__ballot(has));
-        if (l == 0) s_rank[k] = r;
-      }
-      if (HT) {
-        for (int n = 0; n < N; ++n) {
-          if (!((my_nodes >> n) & 1)) continue;
-          const int r = __popcll(__ballot((o_nodes >> n) & 1));
-          if (l == 0) s_rank[KMAX + n] = r;
-        }
-      }
-    }
-    __syncthreads();
-
-    // Positions (uniform), written to the handle's maps.
     int pos[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
+      bool has = false;
+#pragma unroll
+      for (int q = 0; q < KMAX; ++q) has |= ook[q] && oe[q] == me[k];
+      const int rank = __popcll(__ballot(has));
       pos[k] = -1;
       if (mok[k]) {
-        const int pre = p.hist_e[static_cast<int64_t>(j) * E + me[k]] + s_rank[k];
+        const int pre = p.hist_e[static_cast<int64_t>(j) * E + me[k]] + rank;
         pos[k] = HT ? pre : (me[k] * p.S + s) * p.slots + pre;
       }
     }
-    if (c < K) {
+    // Stage-1 row of destination node n (uniform), or -1.
+    auto node_pos = [&](int n) -> int {
+      if (!((my_nodes >> n) & 1)) return -1;
+      return p.hist_n[static_cast<int64_t>(j) * N + n] + __popcll(__ballot((o_nodes >> n) & 1));
+    };
+
+    // 3. The handle's maps (written by the token's first wave).
+    if (part == 0 && lane < K) {
       int v = -1;
 #pragma unroll
       for (int k = 0; k < KMAX; ++k)
-        if (k == c) v = pos[k];
-      (HT ? p.row2 : p.slot_map)[i * K + c] = v;
+        if (k == lane) v = pos[k];
+      (HT ? p.row2 : p.slot_map)[i * K + lane] = v;
     }
-    // Stage-1 row of destination node n (uniform), or -1.
-    auto node_pos = [&](int n) -> int {
-      return ((my_nodes >> n) & 1) ? p.hist_n[static_cast<int64_t>(j) * N + n] + s_rank[KMAX + n] : -1;
-    };
-    if constexpr (HT) {
-      for (int n = c; n < N; n += blockDim.x) p.node_row[i * N + n] = node_pos(n);
+    if (HT && part == 0) {
+      for (int n = 0; n < N; ++n) {
+        const int r = node_pos(n);
+        if (lane == (n & 63)) p.node_row[i * N + n] = r;
+      }
     }
 
     if constexpr (PAYLOAD) {
-      if constexpr (IN == 0) quantize(raw);
-      if constexpr (IN != 1) gather_scales(raw);
-      if constexpr (HT) {
-        for (int n = 0; n < N; ++n) {
-          if (!((my_nodes >> n) & 1)) continue;
-          const int32_t r = node_pos(n);
-          if (IN != 1 || active) put_row<IN>(p, raw, p.st1 + static_cast<int64_t>(r) * p.row_bytes, c, C);
-          if (c == 0) {
+      // 4. Stage-1 destinations as a per-entry list: entry k carries the row
+      //    of its node if it is the token's first entry on that node.
+      int row1[KMAX];
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        row1[k] = -1;
+        if (HT && mok[k]) {
+          const int nk = me[k] / p.P;
+          bool first = true;
+#pragma unroll
+          for (int q = 0; q < k; ++q) first &= !(mok[q] && me[q] / p.P == nk);
+          if (first) row1[k] = node_pos(nk);
+        }
+      }
+      // 5. Metadata of every row (the token's first wave).
+      if (part != 0) {
+      } else if constexpr (HT) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          const int32_t r = row1[k];
+          if (r < 0) continue;
+          if (lane == 0) {
             p.m1_tok[r] = t;
             p.m1_src[r] = s;
           }
-          for (int k = c; k < K; k += blockDim.x) {
+          if (lane < K) {
             int ev = -1;
 #pragma unroll
             for (int q = 0; q < KMAX; ++q)
-              if (q == k) ev = me[q];
-            p.m1_topk[static_cast<int64_t>(r) * K + k] = ev;
-            if (p.w) p.m1_w[static_cast<int64_t>(r) * K + k] = p.w[i * K + k];
+              if (q == lane) ev = me[q];
+            p.m1_topk[static_cast<int64_t>(r) * K + lane] = ev;
+            if (p.w) p.m1_w[static_cast<int64_t>(r) * K + lane] = p.w[i * K + lane];
           }
         }
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           const int32_t r = pos[k];
-          if (r < 0) continue;
-          if (IN != 1 || active) put_row<IN>(p, raw, p.st2 + static_cast<int64_t>(r) * p.row_bytes, c, C);
-          if (c == 0) {
+          if (r >= 0 && lane == 0) {
             p.m2_src[r] = s;
             p.m2_tok[r] = t;
             p.m2_k[r] = k;
@@ -279,50 +290,73 @@ __global__ __launch_bounds__(1024) void dispatch_kernel(DispatchArgs p) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           const int32_t slot = pos[k];
-          if (slot < 0) continue;
-          uint8_t* msg = p.ll_buf + static_cast<int64_t>(slot) * p.msg_bytes;
-          if (IN != 1 || active) put_row<IN>(p, raw, msg, c, C);
-          if (c == 0) {
+          if (slot >= 0 && lane == 0) {
             const i32x4 hdr{t, s, k, 0};
-            __builtin_nontemporal_store(hdr, reinterpret_cast<i32x4*>(msg + p.row_bytes));
+            __builtin_nontemporal_store(hdr, reinterpret_cast<i32x4*>(p.ll_buf + static_cast<int64_t>(slot) * p.msg_pitch + p.row_bytes));
           }
         }
       }
+      // 6. Chunk by chunk: quantise, then store to every destination row, so
+      //    only one chunk's codes are live besides the in-flight loads.
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const int c = c0 + v * 64;
+        if constexpr (IN == 0) quantize(raw[v]);
+        if constexpr (IN != 1) gather_scales(raw[v], lane);
+        if constexpr (HT) {
+#pragma unroll
+          for (int k = 0; k < KMAX; ++k)
+            if (row1[k] >= 0) put_chunk<IN>(p, raw[v], p.st1 + static_cast<int64_t>(row1[k]) * p.row_pitch, c, C);
+#pragma unroll
+          for (int k = 0; k < KMAX; ++k)
+            if (pos[k] >= 0) put_chunk<IN>(p, raw[v], p.st2 + static_cast<int64_t>(pos[k]) * p.row_pitch, c, C);
+        } else {
+#pragma unroll
+          for (int k = 0; k < KMAX; ++k)
+            if (pos[k] >= 0) put_chunk<IN>(p, raw[v], p.ll_buf + static_cast<int64_t>(pos[k]) * p.msg_pitch, c, C);
+        }
+      }
     }
-    __syncthreads();   // s_rank is reused by the next token of this workgroup
   }
 }
 
+// Chunks per lane in one wave's share of a token: enough memory-level
+// parallelism per wave while keeping the wave's registers low enough for
+// full occupancy; a token spans W = ceil(C / (64*NV)) waves.
+constexpr int kChunksPerLane = 2;
+
+template <int IN, bool PAYLOAD, int KMAX, int NV>
+void launch_nv(const DispatchArgs& p, hipStream_t stream) {
+  const int C = p.H / 16;
+  const int W = PAYLOAD ? (C + 64 * NV - 1) / (64 * NV) : 1;
+  int64_t blocks = (p.n * W + 3) / 4;
+  if (p.max_blocks > 0 && blocks > p.max_blocks) blocks = p.max_blocks;
+  if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  if (p.ht) dispatch_kernel<IN, true, PAYLOAD, KMAX, NV><<<grid, block, 0, stream>>>(p, W);
+  else dispatch_kernel<IN, false, PAYLOAD, KMAX, NV><<<grid, block, 0, stream>>>(p, W);
+}
+
 template <int IN, bool PAYLOAD, int KMAX>
-void launch_k(const DispatchArgs& p, dim3 grid, dim3 block, hipStream_t stream) {
-  if (p.ht) dispatch_kernel<IN, true, PAYLOAD, KMAX><<<grid, block, 0, stream>>>(p);
-  else dispatch_kernel<IN, false, PAYLOAD, KMAX><<<grid, block, 0, stream>>>(p);
+void launch_k(const DispatchArgs& p, hipStream_t stream) {
+  if constexpr (!PAYLOAD) launch_nv<IN, PAYLOAD, KMAX, 1>(p, stream);
+  else launch_nv<IN, PAYLOAD, KMAX, kChunksPerLane>(p, stream);
 }
 
 template <int IN, bool PAYLOAD>
-void launch_in(const DispatchArgs& p, dim3 grid, dim3 block, hipStream_t stream) {
-  if (p.K <= 8) launch_k<IN, PAYLOAD, 8>(p, grid, block, stream);
-  else launch_k<IN, PAYLOAD, 32>(p, grid, block, stream);
+void launch_in(const DispatchArgs& p, hipStream_t stream) {
+  if (p.K <= 8) launch_k<IN, PAYLOAD, 8>(p, stream);
+  else launch_k<IN, PAYLOAD, 32>(p, stream);
 }
 
 }  // namespace
 
 hipError_t launch_dispatch(const DispatchArgs& p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;
-  int64_t blocks = p.n;
-  if (p.max_blocks > 0 && blocks > p.max_blocks) blocks = p.max_blocks;
-  if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
-  const dim3 grid(static_cast<unsigned>(blocks));
-  if (!p.payload) {
-    // Maps only: one wave per token.
-    launch_in<0, false>(p, grid, dim3(64), stream);
-    return hipGetLastError();
-  }
-  const int C = p.H / 16;
-  const dim3 block(((C + 63) / 64) * 64);
-  if (p.in_fp8) launch_in<2, true>(p, grid, block, stream);
-  else if (p.out_fp8) launch_in<0, true>(p, grid, block, stream);
-  else launch_in<1, true>(p, grid, block, stream);
+  if (!p.payload) launch_in<0, false>(p, stream);      // maps only
+  else if (p.in_fp8) launch_in<2, true>(p, stream);
+  else if (p.out_fp8) launch_in<0, true>(p, stream);
+  else launch_in<1, true>(p, stream);
   return hipGetLastError();
 }
 

@@ -39,6 +39,8 @@ struct Group {
   int fp8 = 1;        // payload is FP8 (else BF16)
   int64_t row_bytes = 0;   // FP8: H + H/128*4; BF16: 2H
   int64_t msg_bytes = 0;   // LL: row_bytes + 16
+  int64_t row_pitch = 0;   // HT row stride in the buffers: row_bytes up to 128 B
+  int64_t msg_pitch = 0;   // LL message stride: msg_bytes up to 128 B
   int64_t n_max = 0;       // S * T_max
   int64_t rows1_max = 0;   // HT stage-1 rows, worst case
   int64_t rows2_max = 0;   // HT stage-2 rows, worst case (n_max * K)
@@ -78,7 +80,6 @@ struct Handle {
   int n_tiles = 0;
   hipStream_t stream = nullptr;
   bool maps_ready = false;       // slot/row maps written (by dispatch)
-  int32_t* done = nullptr;       // last-workgroup counter of the count kernel
   int32_t* topk = nullptr;       // copy of topk_idx [n_max, K]
   int32_t* slot_map = nullptr;   // LL [n_max, K]
   int32_t* ll_count = nullptr;   // LL [E, S]
@@ -125,9 +126,11 @@ struct LayoutArgs {
   int32_t* c2;
   int32_t* off2;
   int32_t* err;
-  int32_t* done;
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
+
+// LDS bytes the HT prefix-scan workgroup needs for S sources of tps tiles.
+size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps);
 
 // Set `count` int32 values to `value` with a small kernel (stream-ordered,
 // capture-safe).
@@ -143,9 +146,11 @@ struct DispatchArgs {
   int64_t n;
   int T, K, N, H, E, S, P, slots, tps;
   int64_t row_bytes, msg_bytes;
+  int64_t row_pitch, msg_pitch;   // strides of HT rows / LL messages in the buffers
   int ht;
   int payload;            // 0 = compute the maps only
-  int max_blocks;         // 0 = one workgroup per token
+  int num_cu;             // CUs to spread the persistent workgroups over
+  int max_blocks;         // 0 = no cap beyond residency
   const int32_t* topk;    // the handle's copy [n, K]
   const int32_t* hist_e;  // tile prefixes [tiles, E]
   const int32_t* hist_n;  // [tiles, N]

@@ -11,11 +11,9 @@
 //            inside an expert.
 //
 // Positions are a stable counting sort split in two:
-//   * here, per tile of 64 tokens of one source (one wave), the tile's
-//     per-expert and per-node counts (LDS counters), then -- in the last
-//     workgroup to finish, found with a device-scope counter, so no kernel
-//     waits on another -- exclusive prefix sums over the tiles, rewritten in
-//     place, and the per-expert / per-rank totals and offsets;
+//   * here, for every tile of 64 tokens of one source, the exclusive prefix
+//     over the earlier tiles of each key's count plus the key's offset, and
+//     the per-expert / per-rank totals and offsets;
 //   * in the dispatch kernel, each token's rank inside its tile (a ballot
 //     over the <= 63 earlier tokens of the tile), added to the tile prefix.
 // Neither half uses atomics on positions, so every map is bit-reproducible.
@@ -85,6 +83,8 @@ __device__ __forceinline__ int rail_tile(int pos, int g, int G, int tps) {
   return (g + (pos / tps) * G) * tps + pos % tps;
 }
 
+constexpr int kScanRegs = 16;      // tile counts a scan thread keeps in registers
+
 // Sum / exclusive-prefix rewrite of values at idx(pos), pos in [p0, p1),
 // 16 independent loads at a time so that the chain costs one round trip per
 // 16 tiles instead of one per tile.
@@ -121,7 +121,6 @@ __device__ __forceinline__ int chunk_prefix(int32_t* base, int p0, int p1, int r
 template <int KMAX>
 __global__ __launch_bounds__(1024) void layout_count_kernel(LayoutArgs a) {
   extern __shared__ int smem[];
-  __shared__ int s_last;
   const int B = blockDim.x, nw = B >> 6;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int E = a.E, N = a.N, K = a.K;
@@ -162,14 +161,15 @@ __global__ __launch_bounds__(1024) void layout_count_kernel(LayoutArgs a) {
       for (int n = lane; n < N; n += 64) a.hist_n[static_cast<int64_t>(j) * N + n] = cnt_n[w * N + n];
   }
 
-  // The last workgroup to finish turns the histograms into prefix sums.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(a.done, 1) == static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
+// One workgroup turns the tile histograms into exclusive prefix sums (the
+// kernel boundary makes the counts of every tile visible; no fences).
+__global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
+  extern __shared__ int smem[];
+  const int B = blockDim.x;
+  const int tid = threadIdx.x;
+  const int E = a.E, N = a.N;
   const int n_tiles = a.n_tiles;
   if (!a.ht) {
     // LL: per (expert, source), prefix over the source's own tiles.
@@ -180,85 +180,124 @@ __global__ __launch_bounds__(1024) void layout_count_kernel(LayoutArgs a) {
           chunk_prefix(a.hist_e, 0, tps, 0, [=](int tt) { return static_cast<int64_t>(src * tps + tt) * E + e; });
     }
   } else {
-    // Experts: the sequence is every tile in order, cut into C chunks.
-    const int C = B / E > 0 ? B / E : 1;
-    const int CL = (n_tiles + C - 1) / C;
-    int* part = smem;                 // [C][E]
-    int* tot = smem + C * E;          // [E]
-    int* scratch = tot + E;           // [nw]
-    for (int x = tid; x < C * E; x += B) {
-      const int e = x % E, c = x / E;
-      const int j0 = c * CL, j1 = min(n_tiles, j0 + CL);
-      part[c * E + e] = chunk_sum(a.hist_e, j0, j1, [=](int jj) { return static_cast<int64_t>(jj) * E + e; });
-    }
-    __syncthreads();
-    for (int e = tid; e < E; e += B) {
-      int run = 0;
-      for (int c = 0; c < C; ++c) {
-        const int v = part[c * E + e];
-        part[c * E + e] = run;
-        run += v;
-      }
-      tot[e] = run;
-      a.c2[e] = run;
-    }
-    __syncthreads();
-    block_exclusive_scan(tot, E, scratch);
-    for (int e = tid; e < E; e += B) a.off2[e] = tot[e];
-    for (int x = tid; x < C * E; x += B) {
-      const int e = x % E, c = x / E;
-      const int j0 = c * CL, j1 = min(n_tiles, j0 + CL);
-      chunk_prefix(a.hist_e, j0, j1, tot[e] + part[c * E + e],
-                   [=](int jj) { return static_cast<int64_t>(jj) * E + e; });
-    }
-    __syncthreads();
+    // HT.  Keys: the E experts (sequence: every tile in order) and the R
+    // stage-1 ranks d = n*G + g (sequence: the tiles of the sources at
+    // position g, tps consecutive tiles per source).  A thread owns one
+    // (key, chunk) of each kind; it walks its chunk with pointer strides
+    // (no divisions in the loops) and keeps up to kScanRegs counts in
+    // registers between the sum and the rewrite.
+    const int G = a.G, R = N * G, tps = a.tps;
+    const int ce = B / E > 0 ? B / E : 1;                 // expert chunks
+    const int cl_e = (n_tiles + ce - 1) / ce;             // tiles per expert chunk
+    const int cr = B / R > 0 ? B / R : 1;                 // rank chunks
+    const int max_rail = ((a.S + G - 1) / G) * tps;
+    const int cl_r = (max_rail + cr - 1) / cr;            // tiles per rank chunk
+    int* part_e = smem;                  // [ce][E]
+    int* part_r = part_e + ce * E;       // [cr][R]
+    int* tot_e = part_r + cr * R;        // [E]
+    int* tot_r = tot_e + E;              // [R]
+    int* scratch = tot_r + R;            // [B/64]
 
-    // Stage-1 keys d = n*G + g: the tiles of the sources at position g.
-    const int G = a.G, R = N * G;
-    const int CR = B / R > 0 ? B / R : 1;
-    int* partr = smem;                // [CR][R]
-    int* totr = smem + CR * R;        // [R]
-    int* scratch2 = totr + R;
-    for (int x = tid; x < CR * R; x += B) {
-      const int d = x % R, c = x / R;
-      const int n = d / G, g = d - n * G;
-      const int nsrc = g < a.S ? (a.S - g + G - 1) / G : 0;
-      const int len = nsrc * a.tps;
-      const int cl = (len + CR - 1) / CR;
-      const int p0 = c * cl, p1 = min(len, p0 + cl);
-      const int tps = a.tps;
-      partr[c * R + d] = chunk_sum(a.hist_n, p0, p1, [=](int pos) {
-        return static_cast<int64_t>(rail_tile(pos, g, G, tps)) * N + n;
-      });
-    }
-    __syncthreads();
-    for (int d = tid; d < R; d += B) {
-      int run = 0;
-      for (int c = 0; c < CR; ++c) {
-        const int v = partr[c * R + d];
-        partr[c * R + d] = run;
-        run += v;
+    // Expert pair (e, c): tiles [c*cl_e, ...), address stride E.
+    const bool has_e = tid < ce * E;
+    const int e = tid % E, ce_i = tid / E;
+    const int je0 = ce_i * cl_e, ne = has_e ? max(0, min(cl_e, n_tiles - je0)) : 0;
+    int32_t* pe = a.hist_e + static_cast<int64_t>(je0) * E + e;
+    // Rank pair (d, c): positions [c*cl_r, ...) of the rail sequence.
+    const bool has_r = tid < cr * R;
+    const int d = tid % R, cr_i = tid / R, n = d / G, g = d - (d / G) * G;
+    const int nsrc = g < a.S ? (a.S - g + G - 1) / G : 0;
+    const int pr0 = cr_i * cl_r, nr = has_r ? max(0, min(cl_r, nsrc * tps - pr0)) : 0;
+    // the first tile of the chunk: source g + (pr0/tps)*G, tile pr0 % tps
+    const int r_src0 = g + (pr0 / tps) * G, r_tt0 = pr0 % tps;
+
+    const bool regs = cl_e <= kScanRegs && cl_r <= kScanRegs;
+    int ve[kScanRegs], vr[kScanRegs];
+    int se = 0, sr = 0;
+    if (regs) {
+#pragma unroll
+      for (int q = 0; q < kScanRegs; ++q) ve[q] = q < ne ? pe[static_cast<int64_t>(q) * E] : 0;
+      int src = r_src0, tt = r_tt0;
+#pragma unroll
+      for (int q = 0; q < kScanRegs; ++q) {
+        vr[q] = q < nr ? a.hist_n[static_cast<int64_t>(src * tps + tt) * N + n] : 0;
+        if (++tt == tps) { tt = 0; src += G; }
       }
-      totr[d] = run;
-      a.c1[d] = run;
+#pragma unroll
+      for (int q = 0; q < kScanRegs; ++q) { se += ve[q]; sr += vr[q]; }
+    } else {
+      for (int q = 0; q < ne; ++q) se += pe[static_cast<int64_t>(q) * E];
+      int src = r_src0, tt = r_tt0;
+      for (int q = 0; q < nr; ++q) {
+        sr += a.hist_n[static_cast<int64_t>(src * tps + tt) * N + n];
+        if (++tt == tps) { tt = 0; src += G; }
+      }
+    }
+    if (has_e) part_e[ce_i * E + e] = se;
+    if (has_r) part_r[cr_i * R + d] = sr;
+    __syncthreads();
+    for (int x = tid; x < E; x += B) {
+      int run = 0;
+      for (int c = 0; c < ce; ++c) {
+        const int t = part_e[c * E + x];
+        part_e[c * E + x] = run;
+        run += t;
+      }
+      tot_e[x] = run;
+      a.c2[x] = run;
+    }
+    for (int x = tid; x < R; x += B) {
+      int run = 0;
+      for (int c = 0; c < cr; ++c) {
+        const int t = part_r[c * R + x];
+        part_r[c * R + x] = run;
+        run += t;
+      }
+      tot_r[x] = run;
+      a.c1[x] = run;
     }
     __syncthreads();
-    block_exclusive_scan(totr, R, scratch2);
-    for (int d = tid; d < R; d += B) a.off1[d] = totr[d];
-    for (int x = tid; x < CR * R; x += B) {
-      const int d = x % R, c = x / R;
-      const int n = d / G, g = d - n * G;
-      const int nsrc = g < a.S ? (a.S - g + G - 1) / G : 0;
-      const int len = nsrc * a.tps;
-      const int cl = (len + CR - 1) / CR;
-      const int p0 = c * cl, p1 = min(len, p0 + cl);
-      const int tps = a.tps;
-      chunk_prefix(a.hist_n, p0, p1, totr[d] + partr[c * R + d], [=](int pos) {
-        return static_cast<int64_t>(rail_tile(pos, g, G, tps)) * N + n;
-      });
+    block_exclusive_scan(tot_e, E, scratch);
+    block_exclusive_scan(tot_r, R, scratch);
+    for (int x = tid; x < E; x += B) a.off2[x] = tot_e[x];
+    for (int x = tid; x < R; x += B) a.off1[x] = tot_r[x];
+    if (has_e) {
+      int run = tot_e[e] + part_e[ce_i * E + e];
+      if (regs) {
+#pragma unroll
+        for (int q = 0; q < kScanRegs; ++q) {
+          if (q < ne) pe[static_cast<int64_t>(q) * E] = run;
+          run += ve[q];
+        }
+      } else {
+        for (int q = 0; q < ne; ++q) {
+          const int h = pe[static_cast<int64_t>(q) * E];
+          pe[static_cast<int64_t>(q) * E] = run;
+          run += h;
+        }
+      }
+    }
+    if (has_r) {
+      int run = tot_r[d] + part_r[cr_i * R + d];
+      int src = r_src0, tt = r_tt0;
+      if (regs) {
+#pragma unroll
+        for (int q = 0; q < kScanRegs; ++q) {
+          if (q < nr) a.hist_n[static_cast<int64_t>(src * tps + tt) * N + n] = run;
+          run += vr[q];
+          if (++tt == tps) { tt = 0; src += G; }
+        }
+      } else {
+        for (int q = 0; q < nr; ++q) {
+          int32_t* p = a.hist_n + static_cast<int64_t>(src * tps + tt) * N + n;
+          const int h = *p;
+          *p = run;
+          run += h;
+          if (++tt == tps) { tt = 0; src += G; }
+        }
+      }
     }
   }
-  if (tid == 0) *a.done = 0;   // ready for the next handle
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t value) {
@@ -267,27 +306,21 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t value) {
     p[x] = value;
 }
 
-int layout_block_threads(int E, int N) {
-  // 16 waves unless the per-wave LDS counters would exceed 64 KiB.
-  int nw = 16;
-  while (nw > 1 && static_cast<int64_t>(nw) * (E + N) * 4 > 65536) nw >>= 1;
-  return nw * 64;
-}
+constexpr int kCountWaves = 4;     // tiles per count workgroup
+constexpr int kScanThreads = 1024;
 
-size_t layout_lds_bytes(int E, int N, int G, int threads) {
-  const int nw = threads / 64;
-  const int R = N * G;
-  const int C = threads / E > 0 ? threads / E : 1;
-  const int CR = threads / R > 0 ? threads / R : 1;
-  size_t ints = static_cast<size_t>(nw) * (E + N);
-  const size_t scan_e = static_cast<size_t>(C) * E + E + nw;
-  const size_t scan_r = static_cast<size_t>(CR) * R + R + nw;
-  if (scan_e > ints) ints = scan_e;
-  if (scan_r > ints) ints = scan_r;
-  return ints * 4;
-}
+size_t count_lds_bytes(int E, int N) { return static_cast<size_t>(kCountWaves) * (E + N) * 4; }
 
 }  // namespace
+
+size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps) {
+  (void)S;
+  (void)tps;
+  const int R = N * G;
+  const int ce = kScanThreads / E > 0 ? kScanThreads / E : 1;
+  const int cr = kScanThreads / R > 0 ? kScanThreads / R : 1;
+  return (static_cast<size_t>(ce) * E + static_cast<size_t>(cr) * R + E + R + kScanThreads / 64) * 4;
+}
 
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t stream) {
   if (count <= 0) return hipSuccess;
@@ -299,12 +332,11 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t
 
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
-  const int threads = layout_block_threads(a.E, a.N);
-  const int nw = threads / 64;
-  const dim3 grid(static_cast<unsigned>((a.n_tiles + nw - 1) / nw)), block(threads);
-  const size_t lds = layout_lds_bytes(a.E, a.N, a.G, threads);
+  const dim3 grid(static_cast<unsigned>((a.n_tiles + kCountWaves - 1) / kCountWaves)), block(kCountWaves * 64);
+  const size_t lds = count_lds_bytes(a.E, a.N);
   if (a.K <= 8) layout_count_kernel<8><<<grid, block, lds, stream>>>(a);
   else layout_count_kernel<32><<<grid, block, lds, stream>>>(a);
+  layout_scan_kernel<<<dim3(1), dim3(kScanThreads), a.ht ? layout_scan_lds_bytes(a.E, a.N, a.G, a.S, a.tps) : 0, stream>>>(a);
   return hipGetLastError();
 }
 

@@ -132,12 +132,12 @@ ep_status_t ensure_device(Group* g, hipStream_t stream) {
   EP_HIP(hipGetDevice(&g->device));
   EP_HIP(hipDeviceGetAttribute(&g->num_cu, hipDeviceAttributeMultiprocessorCount, g->device));
   EP_HIP(launch_fill_i32(g->err, 1, 0, stream));
-  for (Handle* h : g->handles) EP_HIP(launch_fill_i32(h->done, 1, 0, stream));
   g->dev_ready = true;
   return EP_OK;
 }
 
-void fill_view(ep_tensor_t* v, void* data, int32_t dtype, int64_t d0, int64_t d1, int32_t tag) {
+void fill_view(ep_tensor_t* v, void* data, int32_t dtype, int64_t d0, int64_t d1, int32_t tag,
+               int64_t row_stride = 0) {
   std::memset(v, 0, sizeof(*v));
   v->data = data;
   v->dtype = dtype;
@@ -150,7 +150,7 @@ void fill_view(ep_tensor_t* v, void* data, int32_t dtype, int64_t d0, int64_t d1
     v->ndim = 2;
     v->sizes[0] = d0;
     v->sizes[1] = d1;
-    v->strides[0] = d1;
+    v->strides[0] = row_stride > 0 ? row_stride : d1;
     v->strides[1] = 1;
   }
 }
@@ -176,8 +176,11 @@ DispatchArgs dispatch_base(const Handle* h) {
   p.tps = h->tps;
   p.row_bytes = g->row_bytes;
   p.msg_bytes = g->msg_bytes;
+  p.row_pitch = g->row_pitch;
+  p.msg_pitch = g->msg_pitch;
   p.ht = g->cfg.mode == EP_MODE_HT;
-  p.max_blocks = dispatch_block_cap(g);
+  p.num_cu = g->cfg.num_cus > 0 ? g->cfg.num_cus : g->num_cu;
+  p.max_blocks = 0;
   p.topk = h->topk;
   p.hist_e = h->hist_e;
   p.hist_n = h->hist_n;
@@ -233,6 +236,10 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   if (cfg.num_src_ranks > R) return EP_ERR_UNSUPPORTED;
   if (E > kMaxExperts || K > kMaxTopK || N > kMaxNodes || R > kMaxRanks || cfg.hidden > kMaxHidden)
     return EP_ERR_UNSUPPORTED;
+  if (cfg.mode == EP_MODE_HT &&
+      layout_scan_lds_bytes(E, N, cfg.ranks_per_node, cfg.num_src_ranks,
+                            (cfg.max_tokens_per_rank + kLayoutTile - 1) / kLayoutTile) > 65536)
+    return EP_ERR_UNSUPPORTED;   // more tiles than one workgroup's prefix scan holds
   if (cfg.max_handles == 0) cfg.max_handles = 2;
   if (cfg.max_handles > 64) return EP_ERR_UNSUPPORTED;
 
@@ -247,6 +254,8 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   g->fp8 = cfg.payload == EP_DTYPE_FP8_E4M3;
   g->row_bytes = g->fp8 ? cfg.hidden + cfg.hidden / 128 * 4 : static_cast<int64_t>(cfg.hidden) * 2;
   g->msg_bytes = g->row_bytes + 16;
+  g->row_pitch = (g->row_bytes + 127) / 128 * 128;
+  g->msg_pitch = (g->msg_bytes + 127) / 128 * 128;
   const int64_t S = cfg.num_src_ranks, Tm = cfg.max_tokens_per_rank;
   g->n_max = S * Tm;
   // Distinct destination nodes per token: at most min(K, N) for any topk_idx
@@ -259,9 +268,9 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
 
   ep_status_t st = EP_OK;
   if (cfg.mode == EP_MODE_LL) {
-    g->ll_buf = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(E * S * Tm * g->msg_bytes), &st));
+    g->ll_buf = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(E * S * Tm * g->msg_pitch), &st));
   } else if (st == EP_OK) {
-    g->st1 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows1_max * g->row_bytes), &st));
+    g->st1 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows1_max * g->row_pitch), &st));
     if (st == EP_OK) {
       const size_t r1 = static_cast<size_t>(g->rows1_max);
       const size_t bytes = align_up(r1 * 4) * 2 + align_up(r1 * K * 4) * 2;
@@ -275,7 +284,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
       }
     }
     if (st == EP_OK)
-      g->st2 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows2_max * g->row_bytes), &st));
+      g->st2 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows2_max * g->row_pitch), &st));
     if (st == EP_OK) {
       const size_t r2 = static_cast<size_t>(g->rows2_max);
       uint8_t* b = static_cast<uint8_t*>(dev_alloc(g, align_up(r2 * 4) * 3, &st));
@@ -291,7 +300,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   for (int hs = 0; st == EP_OK && hs < cfg.max_handles; ++hs) {
     const size_t nm = static_cast<size_t>(g->n_max);
     const size_t tiles = static_cast<size_t>(g->tiles_max);
-    size_t bytes = align_up(nm * K * 4) + align_up(4);         // topk copy, counter
+    size_t bytes = align_up(nm * K * 4);                       // topk copy
     if (cfg.mode == EP_MODE_LL) {
       bytes += align_up(nm * K * 4) + align_up(static_cast<size_t>(E) * S * 4);
     } else {
@@ -306,7 +315,6 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
     h->in_use = false;
     Carve cv{b};
     h->topk = cv.take<int32_t>(nm * K);
-    h->done = cv.take<int32_t>(1);
     if (cfg.mode == EP_MODE_LL) {
       h->slot_map = cv.take<int32_t>(nm * K);
       h->ll_count = cv.take<int32_t>(static_cast<size_t>(E) * S);
@@ -452,7 +460,6 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.c2 = h->c2;
   a.off2 = h->off2;
   a.err = g->err;
-  a.done = h->done;
   h->maps_ready = (n == 0);
   if (n == 0 && a.ht) {
     // Nothing routed: counts and offsets are zero.
@@ -596,13 +603,13 @@ EP_API ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t* v
   const int64_t slots_total = static_cast<int64_t>(g->cfg.num_experts) * g->cfg.num_src_ranks *
                               g->cfg.max_tokens_per_rank;
   switch (which) {
-    case EP_BUF_LL_RECV: if (!ll) break; fill_view(view, g->ll_buf, EP_DTYPE_U8, slots_total, g->msg_bytes, EP_TAG_TOKENS); return EP_OK;
-    case EP_BUF_HT_STAGE1: if (ll) break; fill_view(view, g->st1, EP_DTYPE_U8, g->rows1_max, g->row_bytes, EP_TAG_TOKENS); return EP_OK;
+    case EP_BUF_LL_RECV: if (!ll) break; fill_view(view, g->ll_buf, EP_DTYPE_U8, slots_total, g->msg_bytes, EP_TAG_TOKENS, g->msg_pitch); return EP_OK;
+    case EP_BUF_HT_STAGE1: if (ll) break; fill_view(view, g->st1, EP_DTYPE_U8, g->rows1_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
     case EP_BUF_HT_STAGE1_TOKEN: if (ll) break; fill_view(view, g->m1_tok, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE1_SRC: if (ll) break; fill_view(view, g->m1_src, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE1_TOPK: if (ll) break; fill_view(view, g->m1_topk, EP_DTYPE_I32, g->rows1_max, K, EP_TAG_TOPK_IDX); return EP_OK;
     case EP_BUF_HT_STAGE1_WEIGHTS: if (ll) break; fill_view(view, g->m1_w, EP_DTYPE_F32, g->rows1_max, K, EP_TAG_TOPK_WEIGHTS); return EP_OK;
-    case EP_BUF_HT_STAGE2: if (ll) break; fill_view(view, g->st2, EP_DTYPE_U8, g->rows2_max, g->row_bytes, EP_TAG_TOKENS); return EP_OK;
+    case EP_BUF_HT_STAGE2: if (ll) break; fill_view(view, g->st2, EP_DTYPE_U8, g->rows2_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
     case EP_BUF_HT_STAGE2_SRC: if (ll) break; fill_view(view, g->m2_src, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE2_TOKEN: if (ll) break; fill_view(view, g->m2_tok, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE2_K: if (ll) break; fill_view(view, g->m2_k, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;

@@ -242,7 +242,8 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  * row = [q: H bytes][scales: H/128 fp32] (7392 B at H = 7168).  A BF16
  * payload row is the H bf16 values (14336 B).
  *   LL message = row + 16-byte header int32 {src_token, src_rank, k, 0}
- *     (7408 / 14352 B), stored at message index (e*S + s)*T_max + slot.
+ *     (7408 / 14352 B), stored at message index (e*S + s)*T_max + slot
+ *     (message i starts at byte i * pitch, pitch = size rounded up to 128).
  *   HT stage 1: row at node_row(i,n), metadata per row: src_token, src_rank,
  *     topk_idx[K], topk_weights[K].  HT stage 2: row at row(i,k), metadata
  *     per row: src_rank, src_token, k.
@@ -251,7 +252,10 @@ ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t *tokens,
                         const ep_tensor_t *scales, const ep_tensor_t *topk_weights,
                         ep_tensor_t *recv_counts, ep_stream_t stream);
 
-/* Group-owned receive buffers, as U8/I32/F32 views (device memory). */
+/* Group-owned receive buffers, as U8/I32/F32 views (device memory).  Rows
+ * and messages start on 128-byte boundaries: the U8 views' row stride
+ * (strides[0]) is the row / message size rounded up to 128 bytes, and the
+ * padding bytes are never written. */
 typedef enum {
     EP_BUF_LL_RECV = 0,        /* U8 [E*S*T_max, row+16]                     */
     EP_BUF_HT_STAGE1 = 1,      /* U8 [rows1_max, row]                         */
