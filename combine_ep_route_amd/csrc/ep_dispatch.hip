@@ -14,18 +14,17 @@
 // 64*NV 16-element chunks (lane l: chunks c0 + v*64, v < NV); four waves per
 // 256-thread workgroup and no barriers -- each wave ranks its token itself.
 //  1. The token's payload loads are issued first (16-byte loads).
-//  2. Its rank inside its 64-token tile: lane l looks at the l-th earlier
-//     token of the tile and one ballot per entry (and per destination node)
-//     counts the earlier tokens sharing it; adding the tile prefix from the
-//     handle gives every slot / row.  Positions are wave-uniform.
+//  2. Its rank inside its 64-token tile (from the handle) plus the tile's
+//     prefix gives every slot / row.  Positions are wave-uniform.
 //  3. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 and q = E4M3(x/scale),
 //     both IEEE fp32 divisions (round to nearest even).
 //  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
 //     size rounded up to 128 B; the padding is never written).  Each chunk
 //     of codes goes to every destination row with non-temporal stores
-//     (nothing on this GPU reads the rows back during the pass); each
-//     half-wave writes its 4 block scales with one 16-byte store.
+//     (nothing on this GPU reads the rows back during the pass); the
+//     wave's block scales are gathered into its first lanes and written by
+//     one store instruction (16 bytes per 4 blocks).
 #include "ep_internal.h"
 
 namespace ep {
@@ -66,7 +65,6 @@ __device__ __forceinline__ void store_nt(u32x4 v, uint8_t* p) {
 struct Raw {
   u32x4 a, b;
   float scale;   // this lane's block scale
-  u32x4 sc4;     // lanes 0 and 32: the scales of their half-wave's 4 blocks
 };
 
 template <int IN>  // 0: BF16 in -> FP8, 1: BF16 in -> BF16, 2: FP8 in -> FP8
@@ -120,31 +118,51 @@ __device__ __forceinline__ void quantize(Raw& r) {
   r.a = out;
 }
 
-// Lanes 0 and 32 collect the scales of the 4 blocks their half-wave covers
-// (lanes +0, +8, +16, +24), so each half-wave writes them with one store.
-__device__ __forceinline__ void gather_scales(Raw& r, int lane) {
-  const int base = lane & 32;
-#pragma unroll
-  for (int q = 0; q < 4; ++q) r.sc4[q] = __float_as_uint(__shfl(r.scale, base + 8 * q, 64));
+// Stores the 16 bytes of codes (or 32 bytes of bf16) of chunk c of a row.
+template <int IN>
+__device__ __forceinline__ void put_codes(const Raw& r, uint8_t* row, int c, int C) {
+  if (c >= C) return;
+  if constexpr (IN == 1) {
+    store_nt(r.a, row + 32 * c);
+    store_nt(r.b, row + 32 * c + 16);
+  } else {
+    store_nt(r.a, row + 16 * c);
+  }
 }
 
-// Stores chunk c of a row: 16 bytes of codes (or 32 of bf16), and the
-// scales -- 16 bytes per half-wave when its 4 blocks all exist, else one
-// 4-byte store per block.
-template <int IN>
-__device__ __forceinline__ void put_chunk(const DispatchArgs& p, const Raw& r, uint8_t* row, int c, int C) {
-  if constexpr (IN == 1) {
-    if (c < C) {
-      store_nt(r.a, row + 32 * c);
-      store_nt(r.b, row + 32 * c + 16);
+// The wave's block scales, gathered so that one store instruction writes
+// them all: lane 2v holds the scales of blocks 8v..8v+3 of the wave's range
+// (chunk v's lanes 0, 8, 16, 24) and lane 2v+1 those of 8v+4..8v+7.
+template <int NV>
+__device__ __forceinline__ u32x4 gather_scales(const Raw (&raw)[NV], int lane) {
+  u32x4 out{0, 0, 0, 0};
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    u32x4 lo, hi;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      lo[q] = __float_as_uint(__shfl(raw[v].scale, 8 * q, 64));
+      hi[q] = __float_as_uint(__shfl(raw[v].scale, 32 + 8 * q, 64));
     }
+    if (lane == 2 * v) out = lo;
+    if (lane == 2 * v + 1) out = hi;
+  }
+  return out;
+}
+
+// Stores the scales of the wave's blocks [b0, b0 + 8*NV): one 16-byte store
+// per 4 blocks when they all exist, else one 4-byte store per block.
+template <int NV>
+__device__ __forceinline__ void put_scales(const DispatchArgs& p, const Raw (&raw)[NV], u32x4 sc, uint8_t* row,
+                                           int b0, int c0, int C, int lane) {
+  if (b0 + 8 * NV <= (C >> 3)) {
+    if (lane < 2 * NV) store_nt(sc, row + p.H + 4 * (b0 + 4 * lane));
   } else {
-    if (c < C) store_nt(r.a, row + 16 * c);
-    const int hb = (c >> 5) << 2;                 // first block of the half-wave
-    if (hb + 4 <= (C >> 3)) {
-      if ((c & 31) == 0) store_nt(r.sc4, row + p.H + 4 * hb);
-    } else if ((c & 7) == 0 && c < C) {
-      __builtin_nontemporal_store(r.scale, reinterpret_cast<float*>(row + p.H + 4 * (c >> 3)));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = c0 + v * 64;
+      if ((c & 7) == 0 && c < C)
+        __builtin_nontemporal_store(raw[v].scale, reinterpret_cast<float*>(row + p.H + 4 * (c >> 3)));
     }
   }
 }
@@ -186,12 +204,10 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
     }
     const int s = static_cast<int>(i / p.T);
     const int t = static_cast<int>(i - static_cast<int64_t>(s) * p.T);
-    const int tt = t / kTile;
-    const int j = s * p.tps + tt;          // tile of this token
-    const int nb = t - tt * kTile;         // earlier tokens in the tile
+    const int j = s * p.tps + t / kTile;   // tile of this token
 
-    // 2. This token's entries (uniform) and its rank inside the tile: lane l
-    //    holds the l-th earlier token of the tile; one ballot per entry/node.
+    // 2. This token's entries (uniform) plus the handle's in-tile ranks and
+    //    tile prefixes give every slot / row (wave-uniform scalar loads).
     int me[KMAX];
     bool mok[KMAX];
     entries<KMAX>(p.topk + i * K, K, E, true, me, mok);
@@ -199,32 +215,19 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if (mok[k]) my_nodes |= 1ull << (me[k] / p.P);
-    const bool present = lane < nb;
-    int oe[KMAX];
-    bool ook[KMAX];
-    entries<KMAX>(p.topk + (i - nb + (present ? lane : 0)) * K, K, E, present, oe, ook);
-    uint64_t o_nodes = 0;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (ook[k]) o_nodes |= 1ull << (oe[k] / p.P);
-
     int pos[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
-      bool has = false;
-#pragma unroll
-      for (int q = 0; q < KMAX; ++q) has |= ook[q] && oe[q] == me[k];
-      const int rank = __popcll(__ballot(has));
       pos[k] = -1;
-      if (mok[k]) {
-        const int pre = p.hist_e[static_cast<int64_t>(j) * E + me[k]] + rank;
+      if (mok[k] && k < K) {
+        const int pre = p.hist_e[static_cast<int64_t>(j) * E + me[k]] + p.rank_e[i * K + k];
         pos[k] = HT ? pre : (me[k] * p.S + s) * p.slots + pre;
       }
     }
     // Stage-1 row of destination node n (uniform), or -1.
     auto node_pos = [&](int n) -> int {
       if (!((my_nodes >> n) & 1)) return -1;
-      return p.hist_n[static_cast<int64_t>(j) * N + n] + __popcll(__ballot((o_nodes >> n) & 1));
+      return p.hist_n[static_cast<int64_t>(j) * N + n] + p.rank_n[i * N + n];
     };
 
     // 3. The handle's maps (written by the token's first wave).
@@ -296,25 +299,31 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
           }
         }
       }
-      // 6. Chunk by chunk: quantise, then store to every destination row, so
-      //    only one chunk's codes are live besides the in-flight loads.
+      // 6. Quantise every chunk, gather the scales, then write each
+      //    destination row with NV code stores and one scale store.
+      if constexpr (IN == 0) {
 #pragma unroll
-      for (int v = 0; v < NV; ++v) {
-        const int c = c0 + v * 64;
-        if constexpr (IN == 0) quantize(raw[v]);
-        if constexpr (IN != 1) gather_scales(raw[v], lane);
-        if constexpr (HT) {
+        for (int v = 0; v < NV; ++v) quantize(raw[v]);
+      }
+      u32x4 sc{0, 0, 0, 0};
+      if constexpr (IN != 1) sc = gather_scales<NV>(raw, lane);
+      const int b0 = part * NV * 8;     // first block of this wave's range
+      auto put_row = [&](uint8_t* row) {
 #pragma unroll
-          for (int k = 0; k < KMAX; ++k)
-            if (row1[k] >= 0) put_chunk<IN>(p, raw[v], p.st1 + static_cast<int64_t>(row1[k]) * p.row_pitch, c, C);
+        for (int v = 0; v < NV; ++v) put_codes<IN>(raw[v], row, c0 + v * 64, C);
+        if constexpr (IN != 1) put_scales<NV>(p, raw, sc, row, b0, c0, C, lane);
+      };
+      if constexpr (HT) {
 #pragma unroll
-          for (int k = 0; k < KMAX; ++k)
-            if (pos[k] >= 0) put_chunk<IN>(p, raw[v], p.st2 + static_cast<int64_t>(pos[k]) * p.row_pitch, c, C);
-        } else {
+        for (int k = 0; k < KMAX; ++k)
+          if (row1[k] >= 0) put_row(p.st1 + static_cast<int64_t>(row1[k]) * p.row_pitch);
 #pragma unroll
-          for (int k = 0; k < KMAX; ++k)
-            if (pos[k] >= 0) put_chunk<IN>(p, raw[v], p.ll_buf + static_cast<int64_t>(pos[k]) * p.msg_pitch, c, C);
-        }
+        for (int k = 0; k < KMAX; ++k)
+          if (pos[k] >= 0) put_row(p.st2 + static_cast<int64_t>(pos[k]) * p.row_pitch);
+      } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (pos[k] >= 0) put_row(p.ll_buf + static_cast<int64_t>(pos[k]) * p.msg_pitch);
       }
     }
   }
@@ -323,7 +332,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
 // Chunks per lane in one wave's share of a token: enough memory-level
 // parallelism per wave while keeping the wave's registers low enough for
 // full occupancy; a token spans W = ceil(C / (64*NV)) waves.
-constexpr int kChunksPerLane = 2;
+constexpr int kChunksPerLane = 4;
 
 template <int IN, bool PAYLOAD, int KMAX, int NV>
 void launch_nv(const DispatchArgs& p, hipStream_t stream) {

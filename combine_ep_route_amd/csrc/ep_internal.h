@@ -81,6 +81,8 @@ struct Handle {
   hipStream_t stream = nullptr;
   bool maps_ready = false;       // slot/row maps written (by dispatch)
   int32_t* topk = nullptr;       // copy of topk_idx [n_max, K]
+  int32_t* rank_e = nullptr;     // [n_max, K] rank of (token, k) inside its tile and expert, or -1
+  int32_t* rank_n = nullptr;     // [n_max, N] HT: rank inside its tile and destination node, or -1
   int32_t* slot_map = nullptr;   // LL [n_max, K]
   int32_t* ll_count = nullptr;   // LL [E, S]
   int32_t* node_row = nullptr;   // HT [n_max, N]
@@ -117,6 +119,8 @@ struct LayoutArgs {
   int32_t* hist_e;
   int32_t* hist_n;
   int32_t* topk_copy;    // [n, K]
+  int32_t* rank_e;       // [n, K] out: in-tile ranks
+  int32_t* rank_n;       // [n, N] out: in-tile node ranks (HT)
   int32_t* slot_map;
   int32_t* ll_count;
   int32_t* node_row;
@@ -152,6 +156,8 @@ struct DispatchArgs {
   int num_cu;             // CUs to spread the persistent workgroups over
   int max_blocks;         // 0 = no cap beyond residency
   const int32_t* topk;    // the handle's copy [n, K]
+  const int32_t* rank_e;  // in-tile ranks [n, K]
+  const int32_t* rank_n;  // in-tile node ranks [n, N]
   const int32_t* hist_e;  // tile prefixes [tiles, E]
   const int32_t* hist_n;  // [tiles, N]
   int32_t* slot_map;      // LL out [n, K]

@@ -14,8 +14,9 @@
 //   * here, for every tile of 64 tokens of one source, the exclusive prefix
 //     over the earlier tiles of each key's count plus the key's offset, and
 //     the per-expert / per-rank totals and offsets;
-//   * in the dispatch kernel, each token's rank inside its tile (a ballot
-//     over the <= 63 earlier tokens of the tile), added to the tile prefix.
+//   * each token's rank inside its tile (64-bit lane masks per key, one wave
+//     per tile), stored in the handle; the dispatch kernel adds rank and
+//     tile prefix.
 // Neither half uses atomics on positions, so every map is bit-reproducible.
 #include "ep_internal.h"
 
@@ -77,12 +78,6 @@ __device__ void block_exclusive_scan(int* v, int count, int* scratch) {
   __syncthreads();
 }
 
-// The tiles of destination key (n, g) for stage 1: tiles of the sources at
-// position g (s = g, g+G, ...), in order.
-__device__ __forceinline__ int rail_tile(int pos, int g, int G, int tps) {
-  return (g + (pos / tps) * G) * tps + pos % tps;
-}
-
 constexpr int kScanRegs = 16;      // tile counts a scan thread keeps in registers
 
 // Sum / exclusive-prefix rewrite of values at idx(pos), pos in [p0, p1),
@@ -119,13 +114,17 @@ __device__ __forceinline__ int chunk_prefix(int32_t* base, int p0, int p1, int r
 }
 
 template <int KMAX>
-__global__ __launch_bounds__(1024) void layout_count_kernel(LayoutArgs a) {
-  extern __shared__ int smem[];
-  const int B = blockDim.x, nw = B >> 6;
+__global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
+  // Per wave (= tile of 64 tokens, lane = token): a 64-bit mask per expert
+  // and per node of the lanes whose token uses it.  popcount(mask) is the
+  // tile's count; popcount(mask & lanes-below) is the token's rank inside
+  // the tile (a valid key occurs at most once per token).
+  extern __shared__ uint64_t masks[];
+  const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
   const int E = a.E, N = a.N, K = a.K;
-  int* cnt_e = smem;              // [nw][E]
-  int* cnt_n = smem + nw * E;     // [nw][N]
+  uint64_t* m_e = masks;              // [nw][E]
+  uint64_t* m_n = masks + nw * E;     // [nw][N]
 
   const int j = blockIdx.x * nw + w;
   const bool tile_ok = j < a.n_tiles;
@@ -134,33 +133,42 @@ __global__ __launch_bounds__(1024) void layout_count_kernel(LayoutArgs a) {
   const bool active = tile_ok && t < a.T;
   const int64_t i = static_cast<int64_t>(s) * a.T + t;
 
-  for (int x = tid; x < nw * (E + N); x += B) smem[x] = 0;
+  for (int x = tid; x < nw * (E + N); x += blockDim.x) masks[x] = 0;
   Entries<KMAX> en;
   en.load(a.topk + (active ? i : 0) * K, K, E, active);
   __syncthreads();
+  const uint64_t bit = 1ull << lane;
+  uint64_t nodes = 0;
   if (active) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if (k < K) a.topk_copy[i * K + k] = en.e[k];
     if (en.bad) atomicOr(a.err, en.bad);
-    uint64_t nodes = 0;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       if (!en.ok[k]) continue;
-      atomicAdd(&cnt_e[w * E + en.e[k]], 1);
+      atomicOr(reinterpret_cast<unsigned long long*>(&m_e[w * E + en.e[k]]), bit);
       nodes |= 1ull << (en.e[k] / a.P);
     }
     if (a.ht)
       for (int n = 0; n < N; ++n)
-        if ((nodes >> n) & 1) atomicAdd(&cnt_n[w * N + n], 1);
+        if ((nodes >> n) & 1) atomicOr(reinterpret_cast<unsigned long long*>(&m_n[w * N + n]), bit);
   }
   __syncthreads();
   if (tile_ok) {
-    for (int e = lane; e < E; e += 64) a.hist_e[static_cast<int64_t>(j) * E + e] = cnt_e[w * E + e];
+    for (int e = lane; e < E; e += 64) a.hist_e[static_cast<int64_t>(j) * E + e] = __popcll(m_e[w * E + e]);
     if (a.ht)
-      for (int n = lane; n < N; n += 64) a.hist_n[static_cast<int64_t>(j) * N + n] = cnt_n[w * N + n];
+      for (int n = lane; n < N; n += 64) a.hist_n[static_cast<int64_t>(j) * N + n] = __popcll(m_n[w * N + n]);
   }
-
+  if (active) {
+    const uint64_t below = bit - 1;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+      if (k < K) a.rank_e[i * K + k] = en.ok[k] ? __popcll(m_e[w * E + en.e[k]] & below) : -1;
+    if (a.ht)
+      for (int n = 0; n < N; ++n)
+        a.rank_n[i * N + n] = ((nodes >> n) & 1) ? __popcll(m_n[w * N + n] & below) : -1;
+  }
 }
 
 // One workgroup turns the tile histograms into exclusive prefix sums (the
@@ -309,7 +317,7 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t value) {
 constexpr int kCountWaves = 4;     // tiles per count workgroup
 constexpr int kScanThreads = 1024;
 
-size_t count_lds_bytes(int E, int N) { return static_cast<size_t>(kCountWaves) * (E + N) * 4; }
+size_t count_lds_bytes(int E, int N) { return static_cast<size_t>(kCountWaves) * (E + N) * 8; }
 
 }  // namespace
 

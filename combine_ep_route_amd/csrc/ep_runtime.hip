@@ -182,6 +182,8 @@ DispatchArgs dispatch_base(const Handle* h) {
   p.num_cu = g->cfg.num_cus > 0 ? g->cfg.num_cus : g->num_cu;
   p.max_blocks = 0;
   p.topk = h->topk;
+  p.rank_e = h->rank_e;
+  p.rank_n = h->rank_n;
   p.hist_e = h->hist_e;
   p.hist_n = h->hist_n;
   p.slot_map = h->slot_map;
@@ -300,7 +302,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   for (int hs = 0; st == EP_OK && hs < cfg.max_handles; ++hs) {
     const size_t nm = static_cast<size_t>(g->n_max);
     const size_t tiles = static_cast<size_t>(g->tiles_max);
-    size_t bytes = align_up(nm * K * 4);                       // topk copy
+    size_t bytes = align_up(nm * K * 4) * 2 + align_up(nm * N * 4);   // topk copy, ranks
     if (cfg.mode == EP_MODE_LL) {
       bytes += align_up(nm * K * 4) + align_up(static_cast<size_t>(E) * S * 4);
     } else {
@@ -315,6 +317,8 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
     h->in_use = false;
     Carve cv{b};
     h->topk = cv.take<int32_t>(nm * K);
+    h->rank_e = cv.take<int32_t>(nm * K);
+    h->rank_n = cv.take<int32_t>(nm * N);
     if (cfg.mode == EP_MODE_LL) {
       h->slot_map = cv.take<int32_t>(nm * K);
       h->ll_count = cv.take<int32_t>(static_cast<size_t>(E) * S);
@@ -451,6 +455,8 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.hist_e = h->hist_e;
   a.hist_n = h->hist_n;
   a.topk_copy = h->topk;
+  a.rank_e = h->rank_e;
+  a.rank_n = h->rank_n;
   a.slot_map = h->slot_map;
   a.ll_count = h->ll_count;
   a.node_row = h->node_row;
