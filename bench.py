@@ -124,6 +124,9 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
                          "eager: every step is enqueued from Python")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference "
+                         "kernel for scaling HBM byte counters), then exit")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
@@ -132,6 +135,16 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 1 << 30,
+                          "bytes_written_per_launch": 1 << 30, "launches": 3}), flush=True)
+        return 0
 
     import combine_ep_route_amd as ep
 
