@@ -17,8 +17,10 @@
 //  2. Its rank inside its 64-token tile (from the handle) plus the tile's
 //     prefix gives every slot / row.  Positions are wave-uniform.
 //  3. A 128-element block is 8 consecutive lanes; its amax is a 3-step
-//     xor-shuffle inside a DPP row.  scale = amax/448 and q = E4M3(x/scale),
-//     both IEEE fp32 divisions (round to nearest even).
+//     xor-shuffle inside a DPP row.  scale = amax/448 (IEEE fp32 division)
+//     and q = E4M3(x/scale), the quotient by a refined reciprocal and one
+//     fused residual correction (equal to the IEEE quotient's codes on the
+//     whole bf16 domain, which the tests sweep).
 //  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
 //     size rounded up to 128 B; the padding is never written).  Each chunk
 //     of codes goes to every destination row with non-temporal stores
@@ -34,25 +36,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kTile = kLayoutTile;
-
-// E4M3 (OCP, max 448) from fp32: nearest, ties to even, saturating, sign of
-// zero kept.  Normal range: round the fp32 mantissa to 3 bits at bit 20
-// (carry propagates into the exponent), then rebias 127 -> 7.  Below 2^-6
-// the codes are multiples of 2^-9, i.e. rint(|v| * 512) (exact scaling).
-__device__ __forceinline__ uint32_t to_e4m3(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t mag = u & 0x7FFFFFFFu;
-  uint32_t code;
-  if (mag >= 0x3C800000u) {  // |v| >= 2^-6
-    const uint32_t r = mag + 0x7FFFFu + ((mag >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-    code = code > 0x7Eu ? 0x7Eu : code;
-  } else {
-    code = static_cast<uint32_t>(__builtin_rintf(__uint_as_float(mag) * 512.0f));
-  }
-  return sign | code;
-}
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -107,12 +90,35 @@ __device__ __forceinline__ void quantize(Raw& r) {
   if (amax != 0.0f) {
     const float scale = amax / 448.0f;
     r.scale = scale;
+    float qv[16];
+    // The quotient x/scale by Markstein's scheme: a Newton step refines the
+    // hardware reciprocal, and one fused residual correction rounds the
+    // quotient.  The sign is copied from x afterwards, so -0 stays -0 as in
+    // the IEEE quotient.  Blocks whose scale is subnormal use the IEEE
+    // division.  Either way the quotient equals the IEEE one for every bf16
+    // input, and |quotient| <= 448 * (1 + 2^-8) < 464 (the saturation tie).
+    if (scale >= 1.17549435e-38f) {
+      float rinv = __builtin_amdgcn_rcpf(scale);
+      rinv = __builtin_fmaf(__builtin_fmaf(-scale, rinv, 1.0f), rinv, rinv);
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const float q0 = f[q] * rinv;
+        const float res = __builtin_fmaf(-q0, scale, f[q]);
+        qv[q] = __builtin_copysignf(__builtin_fmaf(res, rinv, q0), f[q]);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) qv[q] = f[q] / scale;
+    }
+    // OCP E4M3 codes by the hardware conversion: nearest, ties to even, sign
+    // of zero kept; it saturates to 448 up to the tie at 464 (returns NaN
+    // above, which these quotients never reach).  Two codes per instruction,
+    // the second pair of a word going to its upper half.
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      uint32_t w = 0;
-#pragma unroll
-      for (int b = 0; b < 4; ++b) w |= to_e4m3(f[4 * q + b] / scale) << (8 * b);
-      out[q] = w;
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * q], qv[4 * q + 1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(qv[4 * q + 2], qv[4 * q + 3], w, true);
+      out[q] = static_cast<uint32_t>(w);
     }
   }
   r.a = out;
