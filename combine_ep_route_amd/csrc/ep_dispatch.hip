@@ -196,6 +196,9 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
   const int lane = threadIdx.x & 63;
   const int C = p.H / 16;
   const int K = p.K, E = p.E, N = p.N;
+  // Rows end on whole 128-byte lines when the scale bytes (H/32) are whole
+  // 16-byte groups, so the LL header is 16-byte aligned: H % 512 == 0.
+  const bool line_tail = (p.H & 511) == 0;
   const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
   const int64_t total = p.n * W;
   for (int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); gw < total; gw += waves) {
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
             p.m2_k[r] = k;
           }
         }
-      } else {
+      } else if (!line_tail) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
           const int32_t slot = pos[k];
@@ -314,22 +317,40 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
       u32x4 sc{0, 0, 0, 0};
       if constexpr (IN != 1) sc = gather_scales<NV>(raw, lane);
       const int b0 = part * NV * 8;     // first block of this wave's range
-      auto put_row = [&](uint8_t* row) {
+      // The row's tail, from this wave's first scale (FP8) or the end of the
+      // payload (BF16) to the next 128-byte boundary: the scales, the LL
+      // header, then zeros, so that no cache line of a row is written in
+      // part.  The last wave of the token writes it, 16 bytes per lane.
+      const bool tail_here = line_tail && part == W - 1;
+      const int tail_off = IN == 1 ? 2 * p.H : p.H + 4 * b0;
+      const int tail_sc = IN == 1 ? 0 : ((C >> 3) - b0) >> 2;   // 16-byte groups of scales
+      const int tail_end = static_cast<int>(((HT ? p.row_bytes : p.row_bytes + 16) + 127) & ~int64_t{127});
+      const int tail_groups = (tail_end - tail_off) >> 4;
+      auto put_row = [&](uint8_t* row, int k) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) put_codes<IN>(raw[v], row, c0 + v * 64, C);
-        if constexpr (IN != 1) put_scales<NV>(p, raw, sc, row, b0, c0, C, lane);
+        if (tail_here) {
+          if (lane < tail_groups) {
+            u32x4 v{0, 0, 0, 0};
+            if (lane < tail_sc) v = sc;
+            else if (!HT && lane == tail_sc) v = u32x4{static_cast<uint32_t>(t), static_cast<uint32_t>(s), static_cast<uint32_t>(k), 0u};
+            store_nt(v, row + tail_off + 16 * lane);
+          }
+        } else if constexpr (IN != 1) {
+          put_scales<NV>(p, raw, sc, row, b0, c0, C, lane);
+        }
       };
       if constexpr (HT) {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (row1[k] >= 0) put_row(p.st1 + static_cast<int64_t>(row1[k]) * p.row_pitch);
+          if (row1[k] >= 0) put_row(p.st1 + static_cast<int64_t>(row1[k]) * p.row_pitch, k);
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (pos[k] >= 0) put_row(p.st2 + static_cast<int64_t>(pos[k]) * p.row_pitch);
+          if (pos[k] >= 0) put_row(p.st2 + static_cast<int64_t>(pos[k]) * p.row_pitch, k);
       } else {
 #pragma unroll
         for (int k = 0; k < KMAX; ++k)
-          if (pos[k] >= 0) put_row(p.ll_buf + static_cast<int64_t>(pos[k]) * p.msg_pitch);
+          if (pos[k] >= 0) put_row(p.ll_buf + static_cast<int64_t>(pos[k]) * p.msg_pitch, k);
       }
     }
   }

@@ -254,8 +254,11 @@ ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t *tokens,
 
 /* Group-owned receive buffers, as U8/I32/F32 views (device memory).  Rows
  * and messages start on 128-byte boundaries: the U8 views' row stride
- * (strides[0]) is the row / message size rounded up to 128 bytes, and the
- * padding bytes are never written. */
+ * (strides[0]) is the row / message size rounded up to 128 bytes.  When H is
+ * a multiple of 512 the dispatch writes the padding after each row (message)
+ * it fills with zeros, so that every cache line of a row is written whole;
+ * otherwise the padding is never written.  Rows and slots the handle does
+ * not use are never written. */
 typedef enum {
     EP_BUF_LL_RECV = 0,        /* U8 [E*S*T_max, row+16]                     */
     EP_BUF_HT_STAGE1 = 1,      /* U8 [rows1_max, row]                         */
