@@ -13,7 +13,9 @@
 // owns 8 bf16 (16 bytes) of the row; it issues the K gathered 16-byte loads
 // (non-temporal: every expert-output row is read exactly once) before the
 // first multiply-add so that K loads per lane are in flight, then runs the
-// fp32 fma chain in k order and stores 16 bytes of bf16.
+// fp32 fma chain in k order and stores 16 bytes of bf16 (non-temporal too:
+// the output is not read again by this kernel, and streaming stores keep the
+// L2 for the gathered lines).
 #include "ep_internal.h"
 
 namespace ep {
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
       u32x4 o;
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
-      *reinterpret_cast<u32x4*>(a.out + i * a.ld_out + 8 * c) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + i * a.ld_out + 8 * c));
     }
   }
 }
