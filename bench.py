@@ -114,40 +114,132 @@ def cpu_baseline(scores, x, weights, Y, n_tok):
                 seconds=round(dt, 3), tokens_per_s=round(n_tok / dt, 1))
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--num-cus", type=int, default=0, help="CU cap for dispatch/combine (0 = all)")
-    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
-                    help="graph: the step is captured once per input set in a HIP graph and replayed; "
-                         "eager: every step is enqueued from Python")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy three times (the reference "
-                         "kernel for scaling HBM byte counters), then exit")
-    args = ap.parse_args(argv)
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
-        return 2
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        return 2
+def ll_algorithmic_bytes(n_tok, K, H, E, S):
+    """LL step bytes (every entry valid under the node limit):
+    route    : scores n*E*4 read, topk n*K*4 written
+    dispatch : tokens n*H*2 read, topk n*K*4 read, slot map n*K*4 written,
+               counts E*S*4, messages n*K*(H + H/128*4 + 16) written
+    combine  : n*K*H*2 read, weights + slot map 2*n*K*4 read, n*H*2 written
+    """
+    msg = H + H // 128 * 4 + 16
+    route = n_tok * E * 4 + n_tok * K * 4
+    dispatch = n_tok * H * 2 + 2 * n_tok * K * 4 + E * S * 4 + n_tok * K * msg
+    combine = n_tok * K * H * 2 + 2 * n_tok * K * 4 + n_tok * H * 2
+    total = n_tok * E * 4 + dispatch + combine
+    return dict(route=route, dispatch=dispatch, combine=combine, total=total)
 
-    if args.calibrate_copy:
-        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
+
+def ll_cpu_baseline(T=128):
+    """The oracle on one source's share of the LL decode workload (T tokens)."""
+    import oracle
+    w = I.LL_DECODE.with_(num_src_ranks=1, tokens_per_rank=T)
+    scores = I.scores_for(w)
+    xb = I.bf16_bits(I.tokens_for(w))
+    wts = I.normal_weights(T, 8, w.seed)
+    t0 = time.perf_counter()
+    topk = oracle.route(scores, 8, 8, 4)
+    _, slot, _ = oracle.layout_ll(topk, 1, 256, 128)
+    msgs = oracle.pack_ll(xb, T, 8, True, slot, 256 * 128)
+    used = np.unique(slot[slot >= 0])
+    y = np.zeros((256 * 128, 7168), np.uint16)
+    y[used] = oracle.dequant_rows(msgs[used], 7168, True)
+    oracle.combine(y, wts, slot)
+    dt = time.perf_counter() - t0
+    b = ll_algorithmic_bytes(T, 8, 7168, 256, 1)["total"]
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+                sample=f"one source's {T} tokens of the decode workload (route, fixed-slot layout, "
+                       f"FP8 quantise + LL pack, identity expert on the used slots, combine), "
+                       f"{dt:.2f} s single-threaded",
+                seconds=round(dt, 3), tokens_per_s=round(T / dt, 1))
+
+
+def time_steps(step, args, stream, out_of, ep, g):
+    """Warm-up, an eager pass with events around every call (per-call ms),
+    then (graph mode) one captured step per input set, replayed; the graph's
+    output must equal the eager output of the same step."""
+    log(f"[bench] warmup {args.warmup}")
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    assert ep.ep_get_device_error(g) == 0
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log(f"[bench] eager: timing {args.steps} steps with per-call events")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for j in range(args.steps):
+        step(j, events[j])
+    torch.cuda.synchronize()
+    ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
+    assert ep.ep_get_device_error(g) == 0
+    per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(4)]
+                    for j in range(args.steps)])  # ms
+    mean_ms = per.mean(axis=0)
+    ms_per_step = ms_eager
+    if args.mode == "graph":
+        graph = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step(0)            # warm the capture stream
+        torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
-        print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 1 << 30,
-                          "bytes_written_per_launch": 1 << 30, "launches": 3}), flush=True)
-        return 0
+        with torch.cuda.graph(graph, stream=cap):
+            for j in range(N_SETS):
+                step(j)
+        reps = max(1, args.steps // N_SETS)
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        log(f"[bench] graph: timing {reps * N_SETS} steps ({reps} replays)")
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            graph.replay()
+        torch.cuda.synchronize()
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * N_SETS)
+        assert ep.ep_get_device_error(g) == 0
+        ref = out_of(0).clone()
+        step(0)
+        torch.cuda.synchronize()
+        assert torch.equal(ref.view(torch.int16), out_of(0).view(torch.int16))
+    return mean_ms, ms_eager, ms_per_step
 
-    import combine_ep_route_amd as ep
 
+def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok):
+    names = ["route", "handle", "dispatch", "combine"]
+    value = ab["total"] / (ms_per_step * 1e-3) / 1e9
+    dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
+    dom_ms = mean_ms[names.index(dom)]
+    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
+    return {
+        "metric": "dispatch+combine HBM GB/s and tokens/s on 1 MI355X (% of HBM peak)",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "execution": args.mode,
+        "ms_per_step_eager": round(ms_eager, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3 payload / bf16 combine, fp32 accumulate",
+        "data": "synthetic (seeded; page-3 score distribution, N(0,1) tokens and expert outputs)",
+        "config": config,
+        "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": {k: round(float(v), 5) for k, v in zip(names, mean_ms)},
+        "kernel_gbs": {"route": round(ab["route"] / (mean_ms[0] * 1e-3) / 1e9, 1),
+                       "dispatch": round(ab["dispatch"] / (mean_ms[2] * 1e-3) / 1e9, 1),
+                       "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(dom) if traffic_ok else None,
+                     "algorithmic_bytes_per_launch": ab[dom]},
+    }
+
+
+def run_ht(args, ep):
     w = I.HT_PREFILL
     n_tok, E, K, H = w.num_tokens, w.num_experts, w.top_k, w.hidden
     log(f"[bench] building inputs: {n_tok} tokens, hidden {H}, {E} experts, top-{K}")
@@ -189,105 +281,136 @@ def main(argv=None):
             ev[4].record(stream)
         ep.ep_destroy_handle(h)
 
-    log(f"[bench] warmup {args.warmup}")
-    for j in range(args.warmup):
-        step(j)
-    torch.cuda.synchronize()
-    assert ep.ep_get_device_error(g) == 0
-
     # Exact row counts of this routing (the same every step).
+    ep.ep_route(g, sets[0]["scores"], sets[0]["topk"])
     h = ep.ep_create_handle(g, sets[0]["topk"])
     rows2 = ep.ep_handle_get_num_recv(h, -1)
     rows1 = int(ep.ep_handle_get_map(h, ep._abi.EP_MAP_HT_RANK_COUNT).sum().item())
     ep.ep_destroy_handle(h)
     ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E)
 
-    # Eager pass with events around every call: per-kernel durations.
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    log(f"[bench] eager: timing {args.steps} steps with per-call events")
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j in range(args.steps):
-        step(j, events[j])
-    torch.cuda.synchronize()
-    wall_eager = time.perf_counter() - t0
-    assert ep.ep_get_device_error(g) == 0
-    per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(4)]
-                    for j in range(args.steps)])  # ms
-    mean_ms = per.mean(axis=0)
-    names = ["route", "handle", "dispatch", "combine"]
-    ms_eager = wall_eager * 1e3 / args.steps
-
-    ms_per_step = ms_eager
-    if args.mode == "graph":
-        # One graph holds one step per input set; a replay runs N_SETS steps.
-        graph = torch.cuda.CUDAGraph()
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(cap):
-            step(0)            # warm the capture stream
-        torch.cuda.current_stream().wait_stream(cap)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph, stream=cap):
-            for j in range(N_SETS):
-                step(j)
-        reps = max(1, args.steps // N_SETS)
-        for _ in range(3):
-            graph.replay()
-        torch.cuda.synchronize()
-        log(f"[bench] graph: timing {reps * N_SETS} steps ({reps} replays)")
-        t0 = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
-        torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * N_SETS)
-        assert ep.ep_get_device_error(g) == 0
-        # the graph's output equals the eager output of the same step
-        ref = sets[0]["out"].clone()
-        step(0)
-        torch.cuda.synchronize()
-        assert torch.equal(ref.view(torch.int16), sets[0]["out"].view(torch.int16))
-    value = ab["total"] / (ms_per_step * 1e-3) / 1e9
-
-    dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
-    dom_ms = mean_ms[names.index(dom)]
-    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
-    traffic = stored_traffic(dom)
-
-    result = {
-        "metric": "dispatch+combine HBM GB/s and tokens/s on 1 MI355X (% of HBM peak)",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
-        "execution": args.mode,
-        "ms_per_step_eager": round(ms_eager, 5),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8_e4m3 payload / bf16 combine, fp32 accumulate",
-        "data": "synthetic (seeded; page-3 score distribution, N(0,1) tokens and expert outputs)",
-        "config": {"workload": "ht_prefill_4096_plus_combine", "tokens": n_tok, "hidden": H,
-                   "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
-                   "max_nodes_per_token": 4, "stage1_rows": rows1, "stage2_rows": rows2,
-                   "algorithmic_bytes_per_step": ab["total"]},
-        "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
-        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "kernel_ms": {k: round(float(v), 5) for k, v in zip(names, mean_ms)},
-        "kernel_gbs": {"route": round(ab["route"] / (mean_ms[0] * 1e-3) / 1e9, 1),
-                       "dispatch": round(ab["dispatch"] / (mean_ms[2] * 1e-3) / 1e9, 1),
-                       "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "algorithmic_bytes_per_launch": ab[dom]},
-    }
+    mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
+    config = {"workload": "ht_prefill_4096_plus_combine", "tokens": n_tok, "hidden": H,
+              "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
+              "max_nodes_per_token": 4, "stage1_rows": rows1, "stage2_rows": rows2,
+              "algorithmic_bytes_per_step": ab["total"]}
+    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=True)
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on the same workload")
-        cb = cpu_baseline(scores, x, weights, Y, n_tok)
-        result["cpu_baseline"] = cb
+        result["cpu_baseline"] = cpu_baseline(scores, x, weights, Y, n_tok)
     ep.ep_destroy_group(g)
+    return result
+
+
+def run_ll(args, ep, S):
+    """The LL decode path, staged as in the NCCL-EP pipeline: route, handle,
+    dispatch(send_only) + complete, combine(send_only) + complete."""
+    w = I.LL_DECODE.with_(num_src_ranks=S)
+    T, E, K, H = w.tokens_per_rank, w.num_experts, w.top_k, w.hidden
+    n_tok = S * T
+    log(f"[bench] building inputs: {S} sources x {T} tokens, hidden {H}, {E} experts, top-{K}")
+    scores = I.scores_for(w)
+    x = I.tokens_for(w)
+    weights = I.normal_weights(n_tok, K, w.seed)
+    dev = torch.device("cuda")
+    sets = []
+    for j in range(N_SETS):
+        sets.append(dict(scores=torch.from_numpy(scores).to(dev), x=x.to(dev),
+                         topk=torch.empty((n_tok, K), dtype=torch.int32, device=dev),
+                         counts=torch.empty(E, dtype=torch.int32, device=dev),
+                         out=torch.empty((n_tok, H), dtype=torch.bfloat16, device=dev)))
+    w_d = torch.from_numpy(weights).to(dev)
+    # expert outputs at the dispatch geometry [E, S*T_max, H]; only the used
+    # slots are read
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(I.COMBINE.seed)
+    Y_d = torch.empty((E, S * T, H), dtype=torch.bfloat16, device=dev)
+    Y_d.normal_(generator=gen)
+
+    g = ep.ep_create_group(mode="ll", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
+                           max_nodes_per_token=4, hidden=H, max_tokens_per_rank=T,
+                           num_src_ranks=S, payload="fp8", num_cus=args.num_cus)
+    stream = torch.cuda.current_stream()
+
+    def step(j, ev=None):
+        s = sets[j % N_SETS]
+        if ev is not None:
+            ev[0].record(stream)
+        ep.ep_route(g, s["scores"], s["topk"])
+        if ev is not None:
+            ev[1].record(stream)
+        h = ep.ep_create_handle(g, s["topk"])
+        if ev is not None:
+            ev[2].record(stream)
+        ep.ep_dispatch(h, s["x"], recv_counts=s["counts"], send_only=True)
+        ep.ep_complete(h)
+        if ev is not None:
+            ev[3].record(stream)
+        ep.ep_combine(h, Y_d, w_d, s["out"], send_only=True)
+        ep.ep_complete(h)
+        if ev is not None:
+            ev[4].record(stream)
+        ep.ep_destroy_handle(h)
+
+    ab = ll_algorithmic_bytes(n_tok, K, H, E, S)
+    mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
+    config = {"workload": f"ll_decode_{S}x{T}_plus_combine", "tokens": n_tok, "sources": S,
+              "tokens_per_source": T, "hidden": H, "experts": E, "top_k": K, "nodes": 8,
+              "ranks_per_node": 8, "max_nodes_per_token": 4, "slots": T,
+              "algorithmic_bytes_per_step": ab["total"]}
+    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=False)
+    result["us_per_call"] = {k: round(float(v) * 1e3, 2)
+                             for k, v in zip(["route", "handle", "dispatch", "combine"], mean_ms)}
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on one source's share")
+        result["cpu_baseline"] = ll_cpu_baseline(T)
+    ep.ep_destroy_group(g)
+    return result
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--num-cus", type=int, default=0, help="CU cap for dispatch/combine (0 = all)")
+    ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
+                    help="graph: the step is captured once per input set in a HIP graph and replayed; "
+                         "eager: every step is enqueued from Python")
+    ap.add_argument("--workload", choices=["ht_prefill", "ll_decode", "ll_decode_1src"],
+                    default="ht_prefill",
+                    help="ht_prefill: 4096 tokens, HT dispatch + combine (the headline); "
+                         "ll_decode: 64 sources x 128 tokens, staged LL dispatch + combine; "
+                         "ll_decode_1src: one source's 128 tokens")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (the reference "
+                         "kernel for scaling HBM byte counters), then exit")
+    args = ap.parse_args(argv)
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
+              "multi-GPU runs are not part of this build", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 1 << 30,
+                          "bytes_written_per_launch": 1 << 30, "launches": 3}), flush=True)
+        return 0
+
+    import combine_ep_route_amd as ep
+
+    if args.workload == "ht_prefill":
+        result = run_ht(args, ep)
+    else:
+        result = run_ll(args, ep, 64 if args.workload == "ll_decode" else 1)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -92,6 +92,7 @@ class EpConfig(ctypes.Structure):
         ("payload", ctypes.c_int32),
         ("max_handles", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
+        ("ll_buffers", ctypes.c_int32),
         ("alloc_fn", ALLOC_FN),
         ("free_fn", FREE_FN),
         ("alloc_ctx", ctypes.c_void_p),
@@ -112,9 +113,11 @@ SIGNATURES = {
     "ep_destroy_handle": (_S, [_P]),
     "ep_handle_get_num_recv": (_S, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "ep_handle_get_map": (_S, [_P, ctypes.c_int32, _PT]),
-    "ep_dispatch": (_S, [_P, _PT, _PT, _PT, _PT, _P]),
+    "ep_dispatch": (_S, [_P, _PT, _PT, _PT, _PT, ctypes.c_int32, _P]),
     "ep_get_buffer": (_S, [_P, ctypes.c_int32, _PT]),
-    "ep_combine": (_S, [_P, _PT, _PT, _PT, _P]),
+    "ep_handle_get_buffer": (_S, [_P, ctypes.c_int32, _PT]),
+    "ep_combine": (_S, [_P, _PT, _PT, _PT, ctypes.c_int32, _P]),
+    "ep_complete": (_S, [_P, _P]),
     "ep_dequantize_rows": (_S, [_P, _PT, _PT, _P]),
     "ep_status_string": (ctypes.c_char_p, [_S]),
     "ep_get_device_error": (_S, [_P, ctypes.POINTER(ctypes.c_int32)]),

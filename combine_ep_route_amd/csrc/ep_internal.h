@@ -26,6 +26,20 @@ constexpr uint32_t kGroupMagic = 0x45504752u;   // "EPGR"
 constexpr uint32_t kHandleMagic = 0x4550484Eu;  // "EPHN"
 constexpr uint32_t kDeadMagic = 0xDEADDEADu;
 
+struct CombineArgs {
+  const uint16_t* y;      // BF16 rows
+  int64_t ld_y;           // elements
+  int64_t rows;           // rows available in y
+  const float* w;         // [n, K]
+  const int32_t* loc;     // [n, K]
+  int64_t n;
+  int K, H;
+  uint16_t* out;
+  int64_t ld_out;
+  int max_blocks;         // 0 = no cap
+  int32_t* err;
+};
+
 struct Handle;
 
 struct Group {
@@ -50,7 +64,9 @@ struct Group {
   struct Alloc { void* ptr; size_t bytes; };
   std::vector<Alloc> allocs;
   int64_t bytes = 0;
-  uint8_t* ll_buf = nullptr;
+  uint8_t* ll_buf[2] = {nullptr, nullptr};   // LL receive buffers, used in turn
+  int ll_nbuf = 0;
+  int ll_next = 0;                           // buffer the next LL dispatch takes
   uint8_t* st1 = nullptr;
   int32_t* m1_tok = nullptr;
   int32_t* m1_src = nullptr;
@@ -93,6 +109,14 @@ struct Handle {
   int32_t* off2 = nullptr;       // HT [E]
   int32_t* hist_e = nullptr;     // [tiles_max, E] tile counts -> prefixes
   int32_t* hist_n = nullptr;     // [tiles_max, N]
+  int ll_half = -1;              // LL receive buffer of the last dispatch
+
+  // Staged (send_only) operation awaiting ep_complete: at most one.
+  enum { kPendNone = 0, kPendDispatch = 1, kPendCombine = 2 };
+  int pend = kPendNone;
+  int32_t* pend_counts = nullptr;   // dispatch: recv_counts destination (or null)
+  int pend_per_expert = 0;
+  CombineArgs pend_comb{};          // combine: the launch to run
 };
 
 // ---------------------------------------------------------------------------
@@ -135,6 +159,11 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 
 // LDS bytes the HT prefix-scan workgroup needs for S sources of tps tiles.
 size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps);
+
+// Receive stage of a dispatch: copy the [E, S] counters to out, or with
+// per_expert != 0 write their sums over S ([E]).
+hipError_t launch_recv_counts(const int32_t* counts, int E, int S, int per_expert, int32_t* out,
+                              hipStream_t stream);
 
 // Set `count` int32 values to `value` with a small kernel (stream-ordered,
 // capture-safe).
@@ -179,19 +208,6 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
-struct CombineArgs {
-  const uint16_t* y;      // BF16 rows
-  int64_t ld_y;           // elements
-  int64_t rows;           // rows available in y
-  const float* w;         // [n, K]
-  const int32_t* loc;     // [n, K]
-  int64_t n;
-  int K, H;
-  uint16_t* out;
-  int64_t ld_out;
-  int max_blocks;         // 0 = no cap
-  int32_t* err;
-};
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 struct DequantArgs {

@@ -308,6 +308,20 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
   }
 }
 
+// Receive stage of a dispatch: the per-(expert, source) counters [E, S] as
+// they are, or summed over the sources (tokens per expert).
+__global__ void recv_counts_kernel(const int32_t* counts, int E, int S, int per_expert, int32_t* out) {
+  const int x = blockIdx.x * blockDim.x + threadIdx.x;
+  if (per_expert) {
+    if (x >= E) return;
+    int sum = 0;
+    for (int s = 0; s < S; ++s) sum += counts[static_cast<int64_t>(x) * S + s];
+    out[x] = sum;
+  } else if (x < E * S) {
+    out[x] = counts[x];
+  }
+}
+
 __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t value) {
   for (int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; x < count;
        x += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -328,6 +342,14 @@ size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps) {
   const int ce = kScanThreads / E > 0 ? kScanThreads / E : 1;
   const int cr = kScanThreads / R > 0 ? kScanThreads / R : 1;
   return (static_cast<size_t>(ce) * E + static_cast<size_t>(cr) * R + E + R + kScanThreads / 64) * 4;
+}
+
+hipError_t launch_recv_counts(const int32_t* counts, int E, int S, int per_expert, int32_t* out,
+                              hipStream_t stream) {
+  const int items = per_expert ? E : E * S;
+  if (items <= 0) return hipSuccess;
+  recv_counts_kernel<<<dim3((items + 255) / 256), dim3(256), 0, stream>>>(counts, E, S, per_expert, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t stream) {

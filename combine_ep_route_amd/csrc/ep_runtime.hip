@@ -220,7 +220,8 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   if (cfg.mode != EP_MODE_LL && cfg.mode != EP_MODE_HT) return EP_ERR_INVALID_ARGUMENT;
   if (cfg.num_nodes <= 0 || cfg.ranks_per_node <= 0 || cfg.num_experts <= 0 || cfg.top_k <= 0 ||
       cfg.hidden <= 0 || cfg.max_tokens_per_rank <= 0 || cfg.num_src_ranks <= 0 ||
-      cfg.max_nodes_per_token < 0 || cfg.max_handles < 0 || cfg.num_cus < 0)
+      cfg.max_nodes_per_token < 0 || cfg.max_handles < 0 || cfg.num_cus < 0 || cfg.ll_buffers < 0 ||
+      cfg.ll_buffers > 2)
     return EP_ERR_INVALID_ARGUMENT;
   const int64_t R = static_cast<int64_t>(cfg.num_nodes) * cfg.ranks_per_node;
   if (cfg.num_experts % R != 0) return EP_ERR_INVALID_ARGUMENT;
@@ -243,6 +244,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
                             (cfg.max_tokens_per_rank + kLayoutTile - 1) / kLayoutTile) > 65536)
     return EP_ERR_UNSUPPORTED;   // more tiles than one workgroup's prefix scan holds
   if (cfg.max_handles == 0) cfg.max_handles = 2;
+  if (cfg.ll_buffers == 0) cfg.ll_buffers = 2;
   if (cfg.max_handles > 64) return EP_ERR_UNSUPPORTED;
 
   Group* g = new (std::nothrow) Group();
@@ -270,7 +272,9 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
 
   ep_status_t st = EP_OK;
   if (cfg.mode == EP_MODE_LL) {
-    g->ll_buf = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(E * S * Tm * g->msg_pitch), &st));
+    g->ll_nbuf = cfg.ll_buffers;
+    for (int b = 0; st == EP_OK && b < g->ll_nbuf; ++b)
+      g->ll_buf[b] = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(E * S * Tm * g->msg_pitch), &st));
   } else if (st == EP_OK) {
     g->st1 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows1_max * g->row_pitch), &st));
     if (st == EP_OK) {
@@ -467,6 +471,8 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.off2 = h->off2;
   a.err = g->err;
   h->maps_ready = (n == 0);
+  h->ll_half = -1;
+  h->pend = Handle::kPendNone;
   if (n == 0 && a.ht) {
     // Nothing routed: counts and offsets are zero.
     EP_HIP(launch_fill_i32(h->c1, g->R, 0, s));
@@ -488,6 +494,7 @@ EP_API ep_status_t ep_destroy_handle(ep_handle_t handle) {
   Handle* h = reinterpret_cast<Handle*>(handle);
   if (!handle_ok(h)) return EP_ERR_INVALID_ARGUMENT;
   h->in_use = false;
+  h->pend = Handle::kPendNone;   // a staged operation not completed is dropped
   return EP_OK;
 }
 
@@ -541,7 +548,7 @@ EP_API ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tenso
 
 EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, const ep_tensor_t* scales,
                                const ep_tensor_t* topk_weights, ep_tensor_t* recv_counts,
-                               ep_stream_t stream) {
+                               int32_t send_only, ep_stream_t stream) {
   Handle* h = reinterpret_cast<Handle*>(handle);
   if (!handle_ok(h) || !tokens) return EP_ERR_INVALID_ARGUMENT;
   Group* g = h->g;
@@ -559,14 +566,19 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   if (topk_weights && (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) ||
                        !contiguous2d(topk_weights)))
     return EP_ERR_INVALID_ARGUMENT;
+  int per_expert = 0;
   if (recv_counts) {
-    const bool ok = ll ? (check2d(recv_counts, EP_DTYPE_I32, E, S, EP_TAG_TOKENS_PER_EXPERT, false) &&
-                          contiguous2d(recv_counts))
-                       : (recv_counts->dtype == EP_DTYPE_I32 && recv_counts->ndim == 1 &&
-                          recv_counts->sizes[0] == E && recv_counts->strides[0] == 1 && recv_counts->data &&
-                          (recv_counts->tag == EP_TAG_NONE || recv_counts->tag == EP_TAG_TOKENS_PER_EXPERT));
-    if (!ok) return EP_ERR_INVALID_ARGUMENT;
+    const bool one_d = recv_counts->dtype == EP_DTYPE_I32 && recv_counts->ndim == 1 &&
+                       recv_counts->sizes[0] == E && recv_counts->strides[0] == 1 && recv_counts->data &&
+                       (recv_counts->tag == EP_TAG_NONE || recv_counts->tag == EP_TAG_TOKENS_PER_EXPERT);
+    const bool two_d = ll && recv_counts->ndim == 2 &&
+                       check2d(recv_counts, EP_DTYPE_I32, E, S, EP_TAG_TOKENS_PER_EXPERT, false) &&
+                       contiguous2d(recv_counts);
+    if (!one_d && !two_d) return EP_ERR_INVALID_ARGUMENT;
+    per_expert = ll && one_d;
   }
+  if (send_only && !ll) return EP_ERR_UNSUPPORTED;
+  if (h->pend != Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;   // complete the staged one first
   const hipStream_t s = as_stream(stream);
   if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
   h->stream = s;
@@ -581,7 +593,11 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
     p.ld_s = scales->strides[0];
   }
   p.out_fp8 = g->fp8;
-  p.ll_buf = g->ll_buf;
+  int half = -1;
+  if (ll) {
+    half = g->ll_next;
+    p.ll_buf = g->ll_buf[half];
+  }
   p.w = topk_weights ? static_cast<const float*>(topk_weights->data) : nullptr;
   p.st1 = g->st1;
   p.m1_tok = g->m1_tok;
@@ -594,22 +610,32 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   p.m2_k = g->m2_k;
   if (const ep_status_t st = from_hip(launch_dispatch(p, s)); st != EP_OK) return st;
   h->maps_ready = true;
-  if (recv_counts) {
-    const size_t bytes = (ll ? static_cast<size_t>(E) * S : static_cast<size_t>(E)) * sizeof(int32_t);
-    EP_HIP(hipMemcpyAsync(recv_counts->data, ll ? h->ll_count : h->c2, bytes, hipMemcpyDeviceToDevice, s));
+  if (ll) {
+    h->ll_half = half;
+    g->ll_next = (half + 1) % g->ll_nbuf;
   }
+  int32_t* counts_out = recv_counts ? static_cast<int32_t*>(recv_counts->data) : nullptr;
+  if (send_only) {
+    // The receive stage waits for ep_complete.
+    h->pend = Handle::kPendDispatch;
+    h->pend_counts = counts_out;
+    h->pend_per_expert = per_expert;
+    return EP_OK;
+  }
+  if (counts_out)
+    return from_hip(ll ? launch_recv_counts(h->ll_count, E, S, per_expert, counts_out, s)
+                       : launch_recv_counts(h->c2, E, 1, 0, counts_out, s));
   return EP_OK;
 }
 
-EP_API ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t* view) {
-  Group* g = reinterpret_cast<Group*>(group);
-  if (!group_ok(g) || !view) return EP_ERR_INVALID_ARGUMENT;
+namespace {
+ep_status_t buffer_view(Group* g, int32_t which, int ll_half, ep_tensor_t* view) {
   const bool ll = g->cfg.mode == EP_MODE_LL;
   const int K = g->cfg.top_k;
   const int64_t slots_total = static_cast<int64_t>(g->cfg.num_experts) * g->cfg.num_src_ranks *
                               g->cfg.max_tokens_per_rank;
   switch (which) {
-    case EP_BUF_LL_RECV: if (!ll) break; fill_view(view, g->ll_buf, EP_DTYPE_U8, slots_total, g->msg_bytes, EP_TAG_TOKENS, g->msg_pitch); return EP_OK;
+    case EP_BUF_LL_RECV: if (!ll) break; fill_view(view, g->ll_buf[ll_half], EP_DTYPE_U8, slots_total, g->msg_bytes, EP_TAG_TOKENS, g->msg_pitch); return EP_OK;
     case EP_BUF_HT_STAGE1: if (ll) break; fill_view(view, g->st1, EP_DTYPE_U8, g->rows1_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
     case EP_BUF_HT_STAGE1_TOKEN: if (ll) break; fill_view(view, g->m1_tok, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE1_SRC: if (ll) break; fill_view(view, g->m1_src, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
@@ -623,13 +649,29 @@ EP_API ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t* v
   }
   return EP_ERR_INVALID_ARGUMENT;
 }
+}  // namespace
+
+EP_API ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t* view) {
+  Group* g = reinterpret_cast<Group*>(group);
+  if (!group_ok(g) || !view) return EP_ERR_INVALID_ARGUMENT;
+  return buffer_view(g, which, 0, view);
+}
+
+EP_API ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t* view) {
+  Handle* h = reinterpret_cast<Handle*>(handle);
+  if (!handle_ok(h) || !view) return EP_ERR_INVALID_ARGUMENT;
+  const bool ll = h->g->cfg.mode == EP_MODE_LL;
+  if (ll && which == EP_BUF_LL_RECV && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;
+  return buffer_view(h->g, which, ll ? h->ll_half : 0, view);
+}
 
 // ===========================================================================
 // Combine
 // ===========================================================================
 
 EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
-                              const ep_tensor_t* topk_weights, ep_tensor_t* out, ep_stream_t stream) {
+                              const ep_tensor_t* topk_weights, ep_tensor_t* out, int32_t send_only,
+                              ep_stream_t stream) {
   Handle* h = reinterpret_cast<Handle*>(handle);
   if (!handle_ok(h) || !expert_out) return EP_ERR_INVALID_ARGUMENT;
   Group* g = h->g;
@@ -653,6 +695,8 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
   if (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) || !contiguous2d(topk_weights))
     return EP_ERR_INVALID_ARGUMENT;
   if (!check2d(out, EP_DTYPE_BF16, h->n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
+  if (send_only && !ll) return EP_ERR_UNSUPPORTED;
+  if (h->pend != Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;   // complete the staged one first
   const hipStream_t s = as_stream(stream);
   if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
   h->stream = s;
@@ -670,7 +714,29 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
   a.ld_out = out->strides[0];
   a.max_blocks = dispatch_block_cap(g);
   a.err = g->err;
+  if (send_only) {
+    // The gather-reduce is the receive stage: it waits for ep_complete.
+    h->pend = Handle::kPendCombine;
+    h->pend_comb = a;
+    return EP_OK;
+  }
   return from_hip(launch_combine(a, s));
+}
+
+EP_API ep_status_t ep_complete(ep_handle_t handle, ep_stream_t stream) {
+  Handle* h = reinterpret_cast<Handle*>(handle);
+  if (!handle_ok(h) || h->pend == Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;
+  Group* g = h->g;
+  const hipStream_t s = as_stream(stream);
+  if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
+  h->stream = s;
+  const int pend = h->pend;
+  h->pend = Handle::kPendNone;
+  if (pend == Handle::kPendCombine) return from_hip(launch_combine(h->pend_comb, s));
+  if (h->pend_counts)
+    return from_hip(launch_recv_counts(h->ll_count, g->cfg.num_experts, g->cfg.num_src_ranks,
+                                       h->pend_per_expert, h->pend_counts, s));
+  return EP_OK;
 }
 
 // ===========================================================================

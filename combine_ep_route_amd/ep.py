@@ -85,11 +85,12 @@ class Handle:
         self.ptr = ptr
         self.group = group
         self.num_tokens = num_tokens
+        self._staged = None   # tensors a staged (send_only) call still reads
 
 
 def make_config(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=256, top_k=8,
                 max_nodes_per_token=4, hidden=7168, max_tokens_per_rank=128,
-                num_src_ranks=1, payload="fp8", max_handles=0, num_cus=0,
+                num_src_ranks=1, payload="fp8", max_handles=0, num_cus=0, ll_buffers=0,
                 alloc_fn=None, free_fn=None, alloc_ctx=None) -> A.EpConfig:
     c = A.EpConfig()
     c.mode = {"ll": A.EP_MODE_LL, "ht": A.EP_MODE_HT}[mode] if isinstance(mode, str) else mode
@@ -105,6 +106,7 @@ def make_config(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=256, top_k
         if isinstance(payload, str) else payload
     c.max_handles = max_handles
     c.num_cus = num_cus
+    c.ll_buffers = ll_buffers
     c.alloc_fn = alloc_fn if alloc_fn is not None else A.ALLOC_FN()
     c.free_fn = free_fn if free_fn is not None else A.FREE_FN()
     c.alloc_ctx = alloc_ctx
@@ -146,20 +148,31 @@ def ep_destroy_handle(handle: Handle) -> None:
 
 def ep_dispatch(handle: Handle, tokens: torch.Tensor, scales: Optional[torch.Tensor] = None,
                 topk_weights: Optional[torch.Tensor] = None,
-                recv_counts: Optional[torch.Tensor] = None, stream=None) -> None:
+                recv_counts: Optional[torch.Tensor] = None, send_only: bool = False, stream=None) -> None:
     x = desc(tokens, A.EP_TAG_TOKENS)
     sc = desc(scales, A.EP_TAG_SCALES)
     w = desc(topk_weights, A.EP_TAG_TOPK_WEIGHTS)
     rc = desc(recv_counts, A.EP_TAG_TOKENS_PER_EXPERT)
-    _check("ep_dispatch", A.lib().ep_dispatch(handle.ptr, _ref(x), _ref(sc), _ref(w), _ref(rc), _stream(stream)))
+    _check("ep_dispatch", A.lib().ep_dispatch(handle.ptr, _ref(x), _ref(sc), _ref(w), _ref(rc),
+                                              int(bool(send_only)), _stream(stream)))
+    if send_only:
+        handle._staged = (tokens, scales, topk_weights, recv_counts)   # alive until ep_complete
 
 
 def ep_combine(handle: Handle, expert_out: torch.Tensor, topk_weights: torch.Tensor,
-               out: torch.Tensor, stream=None) -> None:
+               out: torch.Tensor, send_only: bool = False, stream=None) -> None:
     y = desc(expert_out, A.EP_TAG_TOKENS)
     w = desc(topk_weights, A.EP_TAG_TOPK_WEIGHTS)
     o = desc(out, A.EP_TAG_TOKENS)
-    _check("ep_combine", A.lib().ep_combine(handle.ptr, _ref(y), _ref(w), _ref(o), _stream(stream)))
+    _check("ep_combine", A.lib().ep_combine(handle.ptr, _ref(y), _ref(w), _ref(o), int(bool(send_only)),
+                                            _stream(stream)))
+    if send_only:
+        handle._staged = (expert_out, topk_weights, out)   # alive until ep_complete
+
+
+def ep_complete(handle: Handle, stream=None) -> None:
+    _check("ep_complete", A.lib().ep_complete(handle.ptr, _stream(stream)))
+    handle._staged = None
 
 
 def ep_dequantize_rows(group: Group, rows: torch.Tensor, y: torch.Tensor, stream=None) -> None:
@@ -226,4 +239,10 @@ def ep_handle_get_map(handle: Handle, which: int) -> torch.Tensor:
 def ep_get_buffer(group: Group, which: int) -> torch.Tensor:
     d = A.EpTensor()
     _check("ep_get_buffer", A.lib().ep_get_buffer(group.ptr, which, ctypes.byref(d)))
+    return _as_torch(d)
+
+
+def ep_handle_get_buffer(handle: Handle, which: int) -> torch.Tensor:
+    d = A.EpTensor()
+    _check("ep_handle_get_buffer", A.lib().ep_handle_get_buffer(handle.ptr, which, ctypes.byref(d)))
     return _as_torch(d)

@@ -122,6 +122,8 @@ typedef struct {
     int32_t payload;             /* EP_DTYPE_FP8_E4M3 or EP_DTYPE_BF16         */
     int32_t max_handles;         /* live handles at once; 0 means 2            */
     int32_t num_cus;             /* cap on CUs used by dispatch/combine; 0=all */
+    int32_t ll_buffers;          /* LL receive buffers used in turn: 1 or 2;
+                                    0 means 2 (double buffering, NCCL-EP LL) */
     /* Optional allocator hooks: both or neither.  alloc_fn returns device
      * memory of at least `bytes` bytes aligned to 256, or NULL. */
     void *(*alloc_fn)(size_t bytes, void *ctx);
@@ -228,6 +230,18 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
 
 /* Send every token to its experts (NCCL-EP ncclEpDispatch) -- here: write
  * it into the group's receive partitions.
+ *
+ * Two stages, as in NCCL-EP (send and receive phases joined by per-(expert,
+ * source) counters).  The send stage quantises and packs every message into
+ * its receive slot; since the partitions are local HBM, the messages land in
+ * their final place.  The receive stage reads the per-(expert, source)
+ * counters into the caller's recv_counts.  With send_only == 0 both stages
+ * run in this call.  With send_only != 0 (LL only, NCCL-EP's staged mode)
+ * only the send stage is enqueued; ep_complete(handle) enqueues the receive
+ * stage, and recv_counts must stay valid until then.  In LL the group keeps
+ * ll_buffers receive buffers and each dispatch takes the next one in turn
+ * (ep_handle_get_buffer returns the handle's); with two, a dispatch may be
+ * in flight while the previous handle is combined.
  *   tokens : BF16 [n, H] (n as in the handle), rows 16-byte aligned; or
  *            FP8_E4M3 [n, H] together with
  *   scales : F32 [n, H/128] (tag SCALES) -- already quantised tokens are
@@ -235,7 +249,10 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  *   topk_weights : optional F32 [n, K]; HT forwards it in the stage-1
  *            metadata.  Ignored in LL.
  *   recv_counts  : optional I32 out, tag TOKENS_PER_EXPERT: LL [E, S]
- *            counts per (expert, source); HT [E] stage-2 rows per expert.
+ *            counts per (expert, source) or [E] tokens per expert; HT [E]
+ *            stage-2 rows per expert.
+ *   send_only : 0, or (LL) enqueue the send stage only; HT returns
+ *            EP_ERR_UNSUPPORTED (the staged mode is an LL feature).
  * With an FP8 payload each 128-element block is quantised as
  *   scale = amax/448 (fp32 division), q = E4M3(x/scale) (fp32 division,
  *   nearest-even, saturating), amax == 0 -> scale 0 and codes 0;
@@ -250,7 +267,8 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  * Stale contents beyond the counts are left in place (never cleared). */
 ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t *tokens,
                         const ep_tensor_t *scales, const ep_tensor_t *topk_weights,
-                        ep_tensor_t *recv_counts, ep_stream_t stream);
+                        ep_tensor_t *recv_counts, int32_t send_only,
+                        ep_stream_t stream);
 
 /* Group-owned receive buffers, as U8/I32/F32 views (device memory).  Rows
  * and messages start on 128-byte boundaries: the U8 views' row stride
@@ -273,6 +291,11 @@ typedef enum {
 } ep_buffer_t;
 ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
 
+/* As ep_get_buffer, but EP_BUF_LL_RECV is the receive buffer the handle's
+ * last dispatch wrote (ep_get_buffer returns the first of the group's LL
+ * buffers).  EP_ERR_INVALID_ARGUMENT for an LL handle not yet dispatched. */
+ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t *view);
+
 /* ----------------------------------------------------------------------- */
 /* Combine (A7)                                                              */
 /* ----------------------------------------------------------------------- */
@@ -287,10 +310,22 @@ ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
  *                  contiguous, rows 16-byte aligned.  A row index >= rows
  *                  sets EP_DEVERR_ROW_RANGE and is skipped.
  *   topk_weights : F32 [n, K] contiguous.
- *   out          : BF16 [n, H], innermost contiguous, rows 16-byte aligned. */
+ *   out          : BF16 [n, H], innermost contiguous, rows 16-byte aligned.
+ *   send_only    : 0, or (LL) NCCL-EP's staged mode: the combine's receive
+ *                  stage (the gather-reduce into out) is enqueued by
+ *                  ep_complete(handle); expert_out, topk_weights and out must
+ *                  stay valid and unchanged until then.  HT returns
+ *                  EP_ERR_UNSUPPORTED.
+ * EP_ERR_INVALID_ARGUMENT if the handle's dispatch still awaits ep_complete. */
 ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t *expert_out,
                        const ep_tensor_t *topk_weights, ep_tensor_t *out,
-                       ep_stream_t stream);
+                       int32_t send_only, ep_stream_t stream);
+
+/* Finish the handle's staged (send_only) dispatch or combine (NCCL-EP
+ * ncclEpComplete): enqueue its receive stage on `stream`.  Stream-ordered:
+ * the outputs are ready when the stream reaches this point.  A handle has at
+ * most one staged operation; EP_ERR_INVALID_ARGUMENT if it has none. */
+ep_status_t ep_complete(ep_handle_t handle, ep_stream_t stream);
 
 /* ----------------------------------------------------------------------- */
 /* Identity expert (test aid and debugging)                                  */

@@ -97,6 +97,7 @@ def _create(cfg):
     dict(mode=7), dict(num_nodes=0), dict(num_experts=100), dict(top_k=0),
     dict(top_k=300), dict(hidden=7000), dict(hidden=200), dict(payload=A.EP_DTYPE_F32),
     dict(max_tokens_per_rank=0), dict(num_src_ranks=0), dict(max_nodes_per_token=-1),
+    dict(ll_buffers=-1), dict(ll_buffers=3),
     dict(max_nodes_per_token=1, top_k=40),          # 1 node x 32 experts < 40
     dict(num_experts=64, max_nodes_per_token=1, top_k=16),  # ceil(16/1)=16 > 8 per node
 ])
@@ -155,6 +156,31 @@ def test_group_memory_matches_layout():
     assert (view.sizes[0], view.sizes[1]) == (256 * 64 * 128, 7408)
     assert A.lib().ep_get_buffer(g, A.EP_BUF_HT_STAGE1, ctypes.byref(view)) == A.EP_ERR_INVALID_ARGUMENT
     A.lib().ep_destroy_group(g)
+
+
+def test_ll_double_buffering_memory():
+    # two receive buffers by default (NCCL-EP LL double buffering), one on request
+    sizes = {}
+    for nbuf in (0, 1, 2):
+        pool = HostPool()
+        st, g = _create(_cfg(pool, mode=A.EP_MODE_LL, num_src_ranks=4, max_tokens_per_rank=32,
+                             ll_buffers=nbuf))
+        assert st == A.EP_OK
+        b = ctypes.c_int64()
+        assert A.lib().ep_group_memory(g, ctypes.byref(b)) == A.EP_OK
+        sizes[nbuf] = b.value
+        A.lib().ep_destroy_group(g)
+        assert not pool.live
+    one_buffer = 256 * 4 * 32 * 7424          # messages at their 128-byte pitch
+    assert sizes[0] == sizes[2]
+    assert sizes[2] - sizes[1] == one_buffer
+
+
+def test_staged_calls_reject_null_handles():
+    lib = A.lib()
+    view = A.EpTensor()
+    assert lib.ep_complete(None, None) == A.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_handle_get_buffer(None, A.EP_BUF_LL_RECV, ctypes.byref(view)) == A.EP_ERR_INVALID_ARGUMENT
 
 
 def _t(data, dtype, sizes, strides=None, tag=A.EP_TAG_NONE):
