@@ -81,6 +81,8 @@ def _declare(l):
     l.orc_dequant_rows.restype = None
     l.orc_combine.argtypes = [_P, _L, _P, _P, _I, _I, _P, _L, _P]
     l.orc_combine.restype = None
+    l.orc_combine_backward.argtypes = [_P, _P, _L, _P, _P, _L, _I, _I, _P, _P, _P]
+    l.orc_combine_backward.restype = None
     l.orc_f32_to_bf16_n.argtypes = [_P, _L, _P]
     l.orc_f32_to_bf16_n.restype = None
     l.orc_e4m3_encode_n.argtypes = [_P, _L, _P]
@@ -270,3 +272,32 @@ def combine(Y_bits: np.ndarray, weights: np.ndarray, loc: np.ndarray,
     out = np.empty((n_out, H), np.uint16)
     lib().orc_combine(_ptr(Y), H, _ptr(w), _ptr(lc), K, H, _ptr(wh), n_out, _ptr(out))
     return out
+
+
+def combine_backward(g_bits: np.ndarray, weights: np.ndarray, loc: np.ndarray, rows: int,
+                     Y_bits: np.ndarray | None = None):
+    """Adjoint of combine.  g bf16 bits [n, H], w f32 [n, K], loc [n, K], Y bf16
+    bits [rows, H] or None -> (dY bf16 bits [rows, H] (rows no entry points
+    at stay 0), dw f64 [n, K] (zeros without Y), sum |g*Y| f64 [n, K])."""
+    g = _c(g_bits, np.uint16)
+    n, H = g.shape
+    w = _c(weights, np.float32)
+    lc = _c(loc, np.int32)
+    K = lc.shape[1]
+    Y = None if Y_bits is None else _c(Y_bits, np.uint16)
+    if Y is not None and Y.shape != (rows, H):
+        raise ValueError("Y must be [rows, H]")
+    dY = np.zeros((rows, H), np.uint16)
+    dw = np.zeros((n, K), np.float64)
+    da = np.zeros((n, K), np.float64)
+    lib().orc_combine_backward(_ptr(g), _ptr(Y), H, _ptr(w), _ptr(lc), n, K, H, _ptr(dY),
+                               _ptr(dw), _ptr(da))
+    return dY, dw, da
+
+
+def dispatch_backward(dRows_bits: np.ndarray, loc: np.ndarray) -> np.ndarray:
+    """Adjoint of dispatch (straight-through FP8): dx[t] = bf16 of the fp32
+    sum over valid k, in k order, of dRows[loc(t,k)] -- combine with unit
+    weights."""
+    return combine(dRows_bits, np.ones(loc.shape, np.float32), loc)
+

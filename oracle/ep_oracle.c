@@ -481,6 +481,55 @@ void orc_combine(const uint16_t *Y, int64_t ld_y, const float *w,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Backward pass: reuse of the forward handle                                */
+/* ------------------------------------------------------------------------ */
+/* [NCCL-EP] usage (training in HT mode): the backward pass walks the layers
+ * in reverse and reuses each layer's handle -- the loss gradient is
+ * dispatched to the experts, the experts run their backward, and the
+ * experts' gradients are combined back to the tokens.  The pages give no
+ * arithmetic for it; the reading here is the adjoint of the forward maps,
+ * with the FP8 quantisation of the forward dispatch taken as the identity
+ * (straight-through):
+ *
+ * combine forward   out[t] = sum_k w[t,k] * Y[loc(t,k)]
+ *   backward        dY[loc(t,k)][h] = bf16( w[t,k] * g[t][h] )  (one fp32
+ *                                     multiply, then bf16 nearest-even)
+ *                   dw[t,k] = sum_h g[t][h] * Y[loc(t,k)][h]
+ * dw is returned in fp64 (products of two bf16 values are exact in fp64),
+ * with sum_h |g * Y| beside it for the fp32 error bound of a device sum.
+ * Entries with loc < 0 write no row and get dw = 0.  dY uses Y's row stride.
+ *
+ * dispatch forward  rows[loc(t,k)] = x[t]
+ *   backward        dx[t] = bf16( sum over valid k, in k order, from +0 )
+ *                   of dRows[loc(t,k)] -- orc_combine with unit weights
+ *                   (fma(1, y, acc) rounds exactly as y + acc). */
+void orc_combine_backward(const uint16_t *g, const uint16_t *Y, int64_t ld_y,
+                          const float *w, const int32_t *loc, int64_t n, int K,
+                          int H, uint16_t *dY, double *dw, double *dw_abs)
+{
+    for (int64_t t = 0; t < n; ++t) {
+        for (int k = 0; k < K; ++k) {
+            const int32_t r = loc[t * K + k];
+            double s = 0.0, a = 0.0;
+            if (r >= 0) {
+                for (int h = 0; h < H; ++h) {
+                    const float gv = orc_bf16_to_f32(g[t * H + h]);
+                    const float prod = w[t * K + k] * gv;
+                    dY[(int64_t)r * ld_y + h] = orc_f32_to_bf16(prod);
+                    if (Y) {
+                        const double p = (double)gv * (double)orc_bf16_to_f32(Y[(int64_t)r * ld_y + h]);
+                        s += p;
+                        a += fabs(p);
+                    }
+                }
+            }
+            if (dw) dw[t * K + k] = s;
+            if (dw_abs) dw_abs[t * K + k] = a;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Array forms of the scalar conversions (for the pins)                      */
 /* ------------------------------------------------------------------------ */
 void orc_f32_to_bf16_n(const float *x, int64_t n, uint16_t *y)
