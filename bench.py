@@ -153,7 +153,7 @@ def ll_cpu_baseline(T=128):
                 seconds=round(dt, 3), tokens_per_s=round(T / dt, 1))
 
 
-def time_steps(step, args, stream, out_of, ep, g):
+def time_steps(step, args, stream, out_of, ep, g, n_calls=4):
     """Warm-up, an eager pass with events around every call (per-call ms),
     then (graph mode) one captured step per input set, replayed; the graph's
     output must equal the eager output of the same step."""
@@ -162,7 +162,7 @@ def time_steps(step, args, stream, out_of, ep, g):
         step(j)
     torch.cuda.synchronize()
     assert ep.ep_get_device_error(g) == 0
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_calls + 1)] for _ in range(args.steps)]
     log(f"[bench] eager: timing {args.steps} steps with per-call events")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -171,7 +171,7 @@ def time_steps(step, args, stream, out_of, ep, g):
     torch.cuda.synchronize()
     ms_eager = (time.perf_counter() - t0) * 1e3 / args.steps
     assert ep.ep_get_device_error(g) == 0
-    per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(4)]
+    per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(n_calls)]
                     for j in range(args.steps)])  # ms
     mean_ms = per.mean(axis=0)
     ms_per_step = ms_eager
@@ -368,6 +368,86 @@ def run_ll(args, ep, S):
     return result
 
 
+def run_ht_backward(args, ep):
+    """The backward pass at the prefill shape, reusing forward handles (NCCL-EP
+    training example): combine adjoint (bf16 row gradients + weight gradients)
+    then dispatch adjoint (token gradients), per step."""
+    w = I.HT_PREFILL
+    n_tok, E, K, H = w.num_tokens, w.num_experts, w.top_k, w.hidden
+    log(f"[bench] building inputs: backward of {n_tok} tokens, hidden {H}, {E} experts, top-{K}")
+    scores = I.scores_for(w)
+    x = I.tokens_for(w)
+    weights = I.normal_weights(n_tok, K, w.seed)
+    dev = torch.device("cuda")
+    g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
+                           max_nodes_per_token=4, hidden=H, max_tokens_per_rank=n_tok,
+                           num_src_ranks=1, payload="fp8", num_cus=args.num_cus, max_handles=N_SETS)
+    w_d = torch.from_numpy(weights).to(dev)
+    rows2 = n_tok * K
+    Y_d = I.normal_bf16(rows2, H, I.COMBINE.seed).to(dev)
+    dY = torch.empty((rows2, H), dtype=torch.bfloat16, device=dev)
+    sets = []
+    for j in range(N_SETS):
+        s = dict(scores=torch.from_numpy(scores).to(dev),
+                 topk=torch.empty((n_tok, K), dtype=torch.int32, device=dev),
+                 grad=I.normal_bf16(n_tok, H, 800 + j).to(dev),
+                 dw=torch.empty((n_tok, K), dtype=torch.float32, device=dev),
+                 out=torch.empty((n_tok, H), dtype=torch.bfloat16, device=dev))
+        # the forward pass that made the handle (not timed)
+        ep.ep_route(g, s["scores"], s["topk"])
+        s["h"] = ep.ep_create_handle(g, s["topk"])
+        ep.ep_dispatch(s["h"], x.to(dev), topk_weights=w_d)
+        sets.append(s)
+    torch.cuda.synchronize()
+    assert ep.ep_handle_get_num_recv(sets[0]["h"], -1) == rows2
+    stream = torch.cuda.current_stream()
+
+    def step(j, ev=None):
+        s = sets[j % N_SETS]
+        if ev is not None:
+            ev[0].record(stream)
+        ep.ep_combine_backward(s["h"], s["grad"], w_d, dY, expert_out=Y_d, grad_weights=s["dw"])
+        if ev is not None:
+            ev[1].record(stream)
+        ep.ep_dispatch_backward(s["h"], dY, s["out"])
+        if ev is not None:
+            ev[2].record(stream)
+
+    cb = n_tok * H * 2 + 2 * rows2 * H * 2 + 3 * n_tok * K * 4
+    db = rows2 * H * 2 + n_tok * K * 4 + n_tok * H * 2
+    mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g,
+                                                n_calls=2)
+    total = cb + db
+    value = total / (ms_per_step * 1e-3) / 1e9
+    dom, dom_b, dom_ms = ("combine_backward", cb, mean_ms[0]) if mean_ms[0] >= mean_ms[1] else \
+        ("dispatch_backward", db, mean_ms[1])
+    achieved = dom_b / (dom_ms * 1e-3) / 1e9
+    result = {
+        "metric": "dispatch+combine HBM GB/s and tokens/s on 1 MI355X (% of HBM peak)",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "execution": args.mode,
+        "ms_per_step_eager": round(ms_eager, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16 gradients, fp32 accumulate",
+        "data": "synthetic (seeded; page-3 score distribution, N(0,1) gradients and expert outputs)",
+        "config": {"workload": "ht_prefill_4096_backward", "tokens": n_tok, "hidden": H, "experts": E,
+                   "top_k": K, "nodes": 8, "ranks_per_node": 8, "max_nodes_per_token": 4,
+                   "rows": rows2, "algorithmic_bytes_per_step": total},
+        "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "kernel_ms": {"combine_backward": round(float(mean_ms[0]), 5),
+                      "dispatch_backward": round(float(mean_ms[1]), 5)},
+        "kernel_gbs": {"combine_backward": round(cb / (mean_ms[0] * 1e-3) / 1e9, 1),
+                       "dispatch_backward": round(db / (mean_ms[1] * 1e-3) / 1e9, 1)},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": dom_b},
+    }
+    for s in sets:
+        ep.ep_destroy_handle(s["h"])
+    ep.ep_destroy_group(g)
+    return result
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -378,11 +458,12 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
                          "eager: every step is enqueued from Python")
-    ap.add_argument("--workload", choices=["ht_prefill", "ll_decode", "ll_decode_1src"],
+    ap.add_argument("--workload", choices=["ht_prefill", "ll_decode", "ll_decode_1src", "ht_backward"],
                     default="ht_prefill",
                     help="ht_prefill: 4096 tokens, HT dispatch + combine (the headline); "
                          "ll_decode: 64 sources x 128 tokens, staged LL dispatch + combine; "
-                         "ll_decode_1src: one source's 128 tokens")
+                         "ll_decode_1src: one source's 128 tokens; "
+                         "ht_backward: the backward pass at the prefill shape on forward handles")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters), then exit")
@@ -409,6 +490,8 @@ def main(argv=None):
 
     if args.workload == "ht_prefill":
         result = run_ht(args, ep)
+    elif args.workload == "ht_backward":
+        result = run_ht_backward(args, ep)
     else:
         result = run_ll(args, ep, 64 if args.workload == "ll_decode" else 1)
     print(json.dumps(result), flush=True)

@@ -8,7 +8,8 @@ and the weighted top-k combine.  This package is its thin Python binding.
 """
 from . import _abi  # noqa: F401
 from .ep import (  # noqa: F401
-    EpError, Group, Handle, desc, ep_combine, ep_complete, ep_create_group, ep_create_handle,
+    EpError, Group, Handle, desc, ep_combine, ep_combine_backward, ep_complete, ep_create_group,
+    ep_create_handle, ep_dispatch_backward,
     ep_dequantize_rows, ep_destroy_group, ep_destroy_handle, ep_dispatch,
     ep_get_buffer, ep_get_device_error, ep_handle_get_buffer, ep_handle_get_map,
     ep_handle_get_num_recv, ep_last_hip_error, ep_route, ep_status_string, make_config,

@@ -118,6 +118,8 @@ SIGNATURES = {
     "ep_handle_get_buffer": (_S, [_P, ctypes.c_int32, _PT]),
     "ep_combine": (_S, [_P, _PT, _PT, _PT, ctypes.c_int32, _P]),
     "ep_complete": (_S, [_P, _P]),
+    "ep_combine_backward": (_S, [_P, _PT, _PT, _PT, _PT, _PT, _P]),
+    "ep_dispatch_backward": (_S, [_P, _PT, _PT, _P]),
     "ep_dequantize_rows": (_S, [_P, _PT, _PT, _P]),
     "ep_status_string": (ctypes.c_char_p, [_S]),
     "ep_get_device_error": (_S, [_P, ctypes.POINTER(ctypes.c_int32)]),

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
         const int k = k0 + b;
         const int32_t r = k < a.K ? a.loc[i * a.K + k] : -1;
         ok[b] = r >= 0 && r < a.rows;
-        wk[b] = k < a.K ? a.w[i * a.K + k] : 0.0f;
+        wk[b] = k < a.K ? (a.w ? a.w[i * a.K + k] : 1.0f) : 0.0f;   // no weights: unit weights
         if (r >= a.rows && c == 0) atomicOr(a.err, EP_DEVERR_ROW_RANGE);
         // each expert-output row is read exactly once: stream it past the caches
         v[b] = (ok[b] && active)
@@ -75,6 +75,82 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(acc[2 * q], acc[2 * q + 1]);
       __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.out + i * a.ld_out + 8 * c));
+    }
+  }
+}
+
+// Backward of the combine, reusing the forward handle's row map.  One
+// workgroup per token (grid-stride); thread c owns chunks c, c + B, ... of 8
+// bf16 of the row.  For every valid entry k of the token:
+//   dY[loc(t,k)] chunk = bf16_rne(w[t,k] * g chunk)   (one fp32 multiply)
+//   dw[t,k] = sum over the row of g * Y[loc(t,k)]     (per-thread fp32 fma
+//             chains, then a fixed-order shuffle/LDS tree: deterministic)
+// The gradient chunk is loaded once and serves all K entries; expert rows
+// and row gradients stream past the caches (non-temporal).
+template <int KMAX>
+__global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a) {
+  __shared__ float red[KMAX][4];
+  const int C = a.H / 8;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
+  for (int64_t i = blockIdx.x; i < a.n; i += gridDim.x) {
+    int32_t r[KMAX];
+    float wk[KMAX], dot[KMAX];
+    bool ok[KMAX];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      r[k] = k < a.K ? a.loc[i * a.K + k] : -1;
+      ok[k] = r[k] >= 0 && r[k] < a.rows;
+      if (k < a.K && r[k] >= a.rows && threadIdx.x == 0) atomicOr(a.err, EP_DEVERR_ROW_RANGE);
+      wk[k] = k < a.K ? a.w[i * a.K + k] : 0.0f;
+      dot[k] = 0.0f;
+    }
+    for (int c = threadIdx.x; c < C; c += blockDim.x) {
+      const u32x4 gv = *reinterpret_cast<const u32x4*>(a.g + i * a.ld_g + 8 * c);
+      float gf[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gf[2 * q] = __uint_as_float(gv[q] << 16);
+        gf[2 * q + 1] = __uint_as_float(gv[q] & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        if (!ok[k]) continue;
+        u32x4 o;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(wk[k] * gf[2 * q], wk[k] * gf[2 * q + 1]);
+        __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.dy + static_cast<int64_t>(r[k]) * a.ld_dy + 8 * c));
+        if (a.y) {
+          const u32x4 yv = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(a.y + static_cast<int64_t>(r[k]) * a.ld_y + 8 * c));
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            dot[k] = __builtin_fmaf(gf[2 * q], __uint_as_float(yv[q] << 16), dot[k]);
+            dot[k] = __builtin_fmaf(gf[2 * q + 1], __uint_as_float(yv[q] & 0xFFFF0000u), dot[k]);
+          }
+        }
+      }
+    }
+    if (a.dw) {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) {
+        if (k < a.K) {
+          float v = dot[k];
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+          if (lane == 0) red[k][wave] = v;
+        }
+      }
+      __syncthreads();
+      if (threadIdx.x < a.K) {
+        float sum = 0.0f;
+        for (int q = 0; q < nwave; ++q) sum += red[threadIdx.x][q];
+        bool valid = false;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (k == static_cast<int>(threadIdx.x)) valid = ok[k];
+        a.dw[i * a.K + threadIdx.x] = valid ? sum : 0.0f;
+      }
+      __syncthreads();
     }
   }
 }
@@ -134,6 +210,23 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   const dim3 grid(col_blocks, static_cast<unsigned>(rows)), block(threads);
   if (a.K <= 8) combine_kernel<8><<<grid, block, 0, stream>>>(a);
   else combine_kernel<8><<<grid, block, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_backward(const CombineBwdArgs& a, hipStream_t stream) {
+  if (a.n == 0) return hipSuccess;
+  const int C = a.H / 8;
+  // at most 4 waves; whole chunks per thread where H allows
+  int threads = 256;
+  for (int cand : {256, 192, 128})
+    if (C % cand == 0) { threads = cand; break; }
+  if (C < threads) threads = ((C + 63) / 64) * 64;
+  int64_t blocks = a.n;
+  if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
+  if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
+  const dim3 grid(static_cast<unsigned>(blocks)), block(threads);
+  if (a.K <= 8) combine_backward_kernel<8><<<grid, block, 0, stream>>>(a);
+  else combine_backward_kernel<32><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 

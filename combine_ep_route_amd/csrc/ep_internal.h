@@ -30,7 +30,7 @@ struct CombineArgs {
   const uint16_t* y;      // BF16 rows
   int64_t ld_y;           // elements
   int64_t rows;           // rows available in y
-  const float* w;         // [n, K]
+  const float* w;         // [n, K], or null for unit weights (dispatch backward)
   const int32_t* loc;     // [n, K]
   int64_t n;
   int K, H;
@@ -209,6 +209,24 @@ struct DispatchArgs {
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
+
+struct CombineBwdArgs {
+  const uint16_t* g;      // BF16 [n, H] gradient of the combine's output
+  int64_t ld_g;           // elements
+  const uint16_t* y;      // BF16 expert-output rows, or null (no dw)
+  int64_t ld_y;
+  uint16_t* dy;           // BF16 row gradients at the dispatch geometry
+  int64_t ld_dy;
+  int64_t rows;           // rows valid in dy (and y)
+  const float* w;         // [n, K]
+  const int32_t* loc;     // [n, K]
+  float* dw;              // [n, K] or null
+  int64_t n;
+  int K, H;
+  int max_blocks;         // 0 = no cap
+  int32_t* err;
+};
+hipError_t launch_combine_backward(const CombineBwdArgs& a, hipStream_t stream);
 
 struct DequantArgs {
   const uint8_t* rows;

@@ -192,6 +192,27 @@ DispatchArgs dispatch_base(const Handle* h) {
   return p;
 }
 
+// An expert-row tensor (expert outputs or their gradients) as 2-D BF16 rows
+// [rows, H]: given as [rows, H], or in LL as [E, S*T_max, H] with a dense
+// middle dimension.  Rows 16-byte aligned, innermost contiguous.
+bool expert_rows(const Group* g, const ep_tensor_t* t, ep_tensor_t* out) {
+  if (!t) return false;
+  *out = *t;
+  if (t->ndim == 3) {
+    if (g->cfg.mode != EP_MODE_LL) return false;
+    const int64_t per_e = static_cast<int64_t>(g->cfg.num_src_ranks) * g->cfg.max_tokens_per_rank;
+    if (t->sizes[0] != g->cfg.num_experts || t->sizes[1] != per_e || t->strides[2] != 1 ||
+        t->strides[0] != t->strides[1] * per_e)
+      return false;
+    out->ndim = 2;
+    out->sizes[0] = t->sizes[0] * per_e;
+    out->sizes[1] = t->sizes[2];
+    out->strides[0] = t->strides[1];
+    out->strides[1] = 1;
+  }
+  return check2d(out, EP_DTYPE_BF16, -1, g->cfg.hidden, EP_TAG_TOKENS, true);
+}
+
 // Make sure the slot / row maps exist (dispatch writes them; without a
 // dispatch, a maps-only pass computes them).
 ep_status_t ensure_maps(Handle* h, hipStream_t stream) {
@@ -677,21 +698,8 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
   Group* g = h->g;
   const int H = g->cfg.hidden, K = g->cfg.top_k;
   const bool ll = g->cfg.mode == EP_MODE_LL;
-  // expert_out: [rows, H], or in LL [E, S*T_max, H] with a dense middle dim.
-  ep_tensor_t y2 = *expert_out;
-  if (expert_out->ndim == 3) {
-    if (!ll) return EP_ERR_INVALID_ARGUMENT;
-    const int64_t per_e = static_cast<int64_t>(g->cfg.num_src_ranks) * g->cfg.max_tokens_per_rank;
-    if (expert_out->sizes[0] != g->cfg.num_experts || expert_out->sizes[1] != per_e ||
-        expert_out->strides[2] != 1 || expert_out->strides[0] != expert_out->strides[1] * per_e)
-      return EP_ERR_INVALID_ARGUMENT;
-    y2.ndim = 2;
-    y2.sizes[0] = expert_out->sizes[0] * per_e;
-    y2.sizes[1] = expert_out->sizes[2];
-    y2.strides[0] = expert_out->strides[1];
-    y2.strides[1] = 1;
-  }
-  if (!check2d(&y2, EP_DTYPE_BF16, -1, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
+  ep_tensor_t y2;
+  if (!expert_rows(g, expert_out, &y2)) return EP_ERR_INVALID_ARGUMENT;
   if (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) || !contiguous2d(topk_weights))
     return EP_ERR_INVALID_ARGUMENT;
   if (!check2d(out, EP_DTYPE_BF16, h->n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
@@ -720,6 +728,83 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
     h->pend_comb = a;
     return EP_OK;
   }
+  return from_hip(launch_combine(a, s));
+}
+
+// ===========================================================================
+// Backward pass (reuse of the forward handle)
+// ===========================================================================
+
+EP_API ep_status_t ep_combine_backward(ep_handle_t handle, const ep_tensor_t* grad_out,
+                                       const ep_tensor_t* expert_out, const ep_tensor_t* topk_weights,
+                                       ep_tensor_t* grad_expert_out, ep_tensor_t* grad_weights,
+                                       ep_stream_t stream) {
+  Handle* h = reinterpret_cast<Handle*>(handle);
+  if (!handle_ok(h)) return EP_ERR_INVALID_ARGUMENT;
+  Group* g = h->g;
+  const int H = g->cfg.hidden, K = g->cfg.top_k;
+  const bool ll = g->cfg.mode == EP_MODE_LL;
+  if (!check2d(grad_out, EP_DTYPE_BF16, h->n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
+  if (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) || !contiguous2d(topk_weights))
+    return EP_ERR_INVALID_ARGUMENT;
+  ep_tensor_t dy2, y2;
+  if (!expert_rows(g, grad_expert_out, &dy2)) return EP_ERR_INVALID_ARGUMENT;
+  if (expert_out && !expert_rows(g, expert_out, &y2)) return EP_ERR_INVALID_ARGUMENT;
+  if (grad_weights && (!expert_out || !check2d(grad_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) ||
+                       !contiguous2d(grad_weights)))
+    return EP_ERR_INVALID_ARGUMENT;
+  if (h->pend != Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = as_stream(stream);
+  if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
+  h->stream = s;
+  if (const ep_status_t st = ensure_maps(h, s); st != EP_OK) return st;
+  CombineBwdArgs a{};
+  a.g = static_cast<const uint16_t*>(grad_out->data);
+  a.ld_g = grad_out->strides[0];
+  a.y = expert_out ? static_cast<const uint16_t*>(y2.data) : nullptr;
+  a.ld_y = expert_out ? y2.strides[0] : 0;
+  a.dy = static_cast<uint16_t*>(dy2.data);
+  a.ld_dy = dy2.strides[0];
+  a.rows = expert_out ? std::min(dy2.sizes[0], y2.sizes[0]) : dy2.sizes[0];
+  a.w = static_cast<const float*>(topk_weights->data);
+  a.loc = ll ? h->slot_map : h->row2;
+  a.dw = grad_weights ? static_cast<float*>(grad_weights->data) : nullptr;
+  a.n = h->n;
+  a.K = K;
+  a.H = H;
+  a.max_blocks = dispatch_block_cap(g);
+  a.err = g->err;
+  return from_hip(launch_combine_backward(a, s));
+}
+
+EP_API ep_status_t ep_dispatch_backward(ep_handle_t handle, const ep_tensor_t* grad_expert_in,
+                                        ep_tensor_t* grad_tokens, ep_stream_t stream) {
+  Handle* h = reinterpret_cast<Handle*>(handle);
+  if (!handle_ok(h)) return EP_ERR_INVALID_ARGUMENT;
+  Group* g = h->g;
+  const int H = g->cfg.hidden;
+  const bool ll = g->cfg.mode == EP_MODE_LL;
+  ep_tensor_t r2;
+  if (!expert_rows(g, grad_expert_in, &r2)) return EP_ERR_INVALID_ARGUMENT;
+  if (!check2d(grad_tokens, EP_DTYPE_BF16, h->n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
+  if (h->pend != Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = as_stream(stream);
+  if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
+  h->stream = s;
+  if (const ep_status_t st = ensure_maps(h, s); st != EP_OK) return st;
+  CombineArgs a{};
+  a.y = static_cast<const uint16_t*>(r2.data);
+  a.ld_y = r2.strides[0];
+  a.rows = r2.sizes[0];
+  a.w = nullptr;   // unit weights: the sum over the token's entries in k order
+  a.loc = ll ? h->slot_map : h->row2;
+  a.n = h->n;
+  a.K = g->cfg.top_k;
+  a.H = H;
+  a.out = static_cast<uint16_t*>(grad_tokens->data);
+  a.ld_out = grad_tokens->strides[0];
+  a.max_blocks = dispatch_block_cap(g);
+  a.err = g->err;
   return from_hip(launch_combine(a, s));
 }
 

@@ -170,6 +170,25 @@ def ep_combine(handle: Handle, expert_out: torch.Tensor, topk_weights: torch.Ten
         handle._staged = (expert_out, topk_weights, out)   # alive until ep_complete
 
 
+def ep_combine_backward(handle: Handle, grad_out: torch.Tensor, topk_weights: torch.Tensor,
+                        grad_expert_out: torch.Tensor, expert_out: Optional[torch.Tensor] = None,
+                        grad_weights: Optional[torch.Tensor] = None, stream=None) -> None:
+    g = desc(grad_out, A.EP_TAG_TOKENS)
+    y = desc(expert_out, A.EP_TAG_TOKENS)
+    w = desc(topk_weights, A.EP_TAG_TOPK_WEIGHTS)
+    dy = desc(grad_expert_out, A.EP_TAG_TOKENS)
+    dw = desc(grad_weights, A.EP_TAG_TOPK_WEIGHTS)
+    _check("ep_combine_backward", A.lib().ep_combine_backward(handle.ptr, _ref(g), _ref(y), _ref(w), _ref(dy),
+                                                              _ref(dw), _stream(stream)))
+
+
+def ep_dispatch_backward(handle: Handle, grad_expert_in: torch.Tensor, grad_tokens: torch.Tensor,
+                         stream=None) -> None:
+    r = desc(grad_expert_in, A.EP_TAG_TOKENS)
+    o = desc(grad_tokens, A.EP_TAG_TOKENS)
+    _check("ep_dispatch_backward", A.lib().ep_dispatch_backward(handle.ptr, _ref(r), _ref(o), _stream(stream)))
+
+
 def ep_complete(handle: Handle, stream=None) -> None:
     _check("ep_complete", A.lib().ep_complete(handle.ptr, _stream(stream)))
     handle._staged = None

@@ -328,6 +328,50 @@ ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t *expert_out,
 ep_status_t ep_complete(ep_handle_t handle, ep_stream_t stream);
 
 /* ----------------------------------------------------------------------- */
+/* Backward pass: reuse of the forward handle                                */
+/* ----------------------------------------------------------------------- */
+
+/* In training the backward pass reuses each layer's handle: the loss
+ * gradient goes to the experts and the experts' gradients come back to the
+ * tokens (NCCL-EP paper notes, usage: HT training example).  These are the
+ * adjoints of ep_combine and ep_dispatch over the handle's row map (the FP8
+ * quantisation of the forward dispatch is taken as the identity).  Neither
+ * uses the receive buffers; both need the handle's maps (written by its
+ * dispatch, or computed on first use) and no staged operation pending
+ * (else EP_ERR_INVALID_ARGUMENT).  Rows that no entry points at are not
+ * written. */
+
+/* Backward of ep_combine.  For every valid entry (i, k) with row
+ * r = row(i,k):
+ *   grad_expert_out[r][h] = bf16_rne(w[i][k] * grad_out[i][h])  (one fp32
+ *                           multiply) -- a BF16 dispatch of the gradient;
+ *   grad_weights[i][k]    = sum over h of grad_out[i][h] * expert_out[r][h]
+ *                           in fp32 (deterministic order; within the fp32
+ *                           dot-product error bound of the exact sum).
+ * Invalid entries write no row and get grad_weights 0.
+ *   grad_out        : BF16 [n, H], rows 16-byte aligned.
+ *   expert_out      : BF16 expert-output rows as for ep_combine, or NULL
+ *                     (then grad_weights must be NULL).
+ *   topk_weights    : F32 [n, K] contiguous.
+ *   grad_expert_out : BF16 rows at the dispatch geometry ([rows, H], or LL
+ *                     [E, S*T_max, H]).
+ *   grad_weights    : optional F32 [n, K] contiguous. */
+ep_status_t ep_combine_backward(ep_handle_t handle, const ep_tensor_t *grad_out,
+                                const ep_tensor_t *expert_out,
+                                const ep_tensor_t *topk_weights,
+                                ep_tensor_t *grad_expert_out,
+                                ep_tensor_t *grad_weights, ep_stream_t stream);
+
+/* Backward of ep_dispatch:
+ *   grad_tokens[i][h] = bf16_rne( fp32 sum over valid k, in k order, from +0,
+ *                                 of grad_expert_in[row(i,k)][h] )
+ * -- the combine with unit weights.
+ *   grad_expert_in : BF16 rows at the dispatch geometry.
+ *   grad_tokens    : BF16 [n, H], rows 16-byte aligned. */
+ep_status_t ep_dispatch_backward(ep_handle_t handle, const ep_tensor_t *grad_expert_in,
+                                 ep_tensor_t *grad_tokens, ep_stream_t stream);
+
+/* ----------------------------------------------------------------------- */
 /* Identity expert (test aid and debugging)                                  */
 /* ----------------------------------------------------------------------- */
 
