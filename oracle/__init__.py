@@ -83,6 +83,10 @@ def _declare(l):
     l.orc_combine.restype = None
     l.orc_combine_backward.argtypes = [_P, _P, _L, _P, _P, _L, _I, _I, _P, _P, _P]
     l.orc_combine_backward.restype = None
+    l.orc_layout_ht_rank.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P]
+    l.orc_layout_ht_rank.restype = _I
+    l.orc_meta_ht_rank.argtypes = [_P, _P, _L, _I, _I, _I, _P, _P, _P]
+    l.orc_meta_ht_rank.restype = None
     l.orc_f32_to_bf16_n.argtypes = [_P, _L, _P]
     l.orc_f32_to_bf16_n.restype = None
     l.orc_e4m3_encode_n.argtypes = [_P, _L, _P]
@@ -300,4 +304,36 @@ def dispatch_backward(dRows_bits: np.ndarray, loc: np.ndarray) -> np.ndarray:
     sum over valid k, in k order, of dRows[loc(t,k)] -- combine with unit
     weights."""
     return combine(dRows_bits, np.ones(loc.shape, np.float32), loc)
+
+
+def layout_ht_rank(topk: np.ndarray, num_src: int, num_experts: int, num_ranks: int):
+    """Stage 2 with one row per (token, destination rank) -> dict(c2 [R],
+    off2 [R], row2 [S*T, K] (row at the token's first entry on each rank,
+    -1 elsewhere), err)."""
+    t = _c(topk, np.int32)
+    n, k = t.shape
+    T = n // num_src
+    c2 = np.empty(num_ranks, np.int32)
+    off2 = np.empty(num_ranks, np.int32)
+    row2 = np.empty((n, k), np.int32)
+    err = np.zeros(1, np.int32)
+    rc = lib().orc_layout_ht_rank(_ptr(t), num_src, T, k, num_experts, num_ranks, _ptr(c2),
+                                  _ptr(off2), _ptr(row2), _ptr(err))
+    if rc != 0:
+        raise ValueError(f"orc_layout_ht_rank failed (rc={rc})")
+    return dict(c2=c2, off2=off2, row2=row2, err=int(err[0]))
+
+
+def meta_ht_rank(topk: np.ndarray, weights, row2: np.ndarray, num_experts: int, num_ranks: int,
+                 rows: int):
+    """Per-rank stage-2 received top-k: (local expert ids or -1 [rows, K],
+    weights or 0 [rows, K])."""
+    t = _c(topk, np.int32)
+    n, K = t.shape
+    mt = np.full((rows, K), -7, np.int32)
+    mw = np.full((rows, K), -7.0, np.float32)
+    w = None if weights is None else _c(weights, np.float32)
+    lib().orc_meta_ht_rank(_ptr(t), _ptr(w), n, K, num_experts, num_ranks, _ptr(_c(row2, np.int32)),
+                           _ptr(mt), _ptr(mw) if w is not None else None)
+    return mt, mw
 

@@ -311,6 +311,82 @@ int orc_layout_ht(const int32_t *topk, int S, int T, int K, int E, int N, int G,
 }
 
 /* ------------------------------------------------------------------------ */
+/* A2 (HT), stage 2 per destination rank  [DeepEP, high-throughput mode]     */
+/* ------------------------------------------------------------------------ */
+/*
+ * The alternative the page's traffic study compares: one copy per
+ * destination GPU.  Stage 2 gets one row per (token, distinct rank
+ * r = e / (E/R) among its valid entries), grouped by rank ascending and
+ * ordered (source, token) inside a rank.  Reading taken: the row belongs to
+ * the token's first entry (k order) on that rank; the token's other entries
+ * on the same rank get -1, so every row appears once in a token's map.
+ *   c2[r], off2[r] (R entries); row2[i*K + k] = global stage-2 row, or -1.
+ * Stage 1 is unchanged (orc_layout_ht).
+ */
+int orc_layout_ht_rank(const int32_t *topk, int S, int T, int K, int E, int R,
+                       int32_t *c2, int32_t *off2, int32_t *row2, int32_t *err)
+{
+    if (R <= 0 || E % R != 0) return -1;
+    const int L = E / R;
+    const int64_t n_tok = (int64_t)S * T;
+    unsigned char *hit = malloc((size_t)R);
+    int32_t *run = calloc((size_t)R, sizeof(int32_t));
+    if (!hit || !run) return -2;
+    memset(c2, 0, sizeof(int32_t) * (size_t)R);
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const int32_t *row = topk + i * K;
+        memset(hit, 0, (size_t)R);
+        int32_t dummy = 0;
+        for (int k = 0; k < K; ++k) {
+            if (!entry_valid(row, k, E, &dummy)) continue;
+            const int r = row[k] / L;
+            if (!hit[r]) { hit[r] = 1; c2[r]++; }
+        }
+    }
+    int32_t acc = 0;
+    for (int r = 0; r < R; ++r) { off2[r] = acc; acc += c2[r]; }
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const int32_t *row = topk + i * K;
+        memset(hit, 0, (size_t)R);
+        for (int k = 0; k < K; ++k) {
+            row2[i * K + k] = -1;
+            if (!entry_valid(row, k, E, err)) continue;
+            const int r = row[k] / L;
+            if (hit[r]) continue;
+            hit[r] = 1;
+            row2[i * K + k] = off2[r] + run[r]++;
+        }
+    }
+    free(hit); free(run);
+    return 0;
+}
+
+/* What a rank receives with each per-rank stage-2 row (DeepEP's received
+ * top-k form): for the token's entry kk, its local expert index
+ * e - r*(E/R) if it is a valid entry on the row's rank r, else -1; and its
+ * weight, else 0 (weights omitted when w is NULL).  Rows are those of
+ * row2 from orc_layout_ht_rank. */
+void orc_meta_ht_rank(const int32_t *topk, const float *w, int64_t n_tok, int K, int E,
+                      int R, const int32_t *row2, int32_t *meta_topk, float *meta_w)
+{
+    const int L = E / R;
+    for (int64_t i = 0; i < n_tok; ++i) {
+        const int32_t *row = topk + i * K;
+        for (int k = 0; k < K; ++k) {
+            const int32_t dst = row2[i * K + k];
+            if (dst < 0) continue;
+            const int r = row[k] / L;
+            for (int kk = 0; kk < K; ++kk) {
+                int32_t dummy = 0;
+                const int here = entry_valid(row, kk, E, &dummy) && row[kk] / L == r;
+                meta_topk[(int64_t)dst * K + kk] = here ? row[kk] - r * L : -1;
+                if (meta_w) meta_w[(int64_t)dst * K + kk] = here ? w[i * K + kk] : 0.0f;
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
 /* A3  FP8 E4M3 quantisation, one fp32 scale per 128 elements  [DeepEP]      */
 /* ------------------------------------------------------------------------ */
 /*
