@@ -48,7 +48,7 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(n_tok, K, H, rows1, rows2, E):
+def algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank=False):
     """Bytes each step must move at least once (read + write), per kernel.
 
     route    : scores n*E*4 read, topk n*K*4 written
@@ -59,12 +59,15 @@ def algorithmic_bytes(n_tok, K, H, rows1, rows2, E):
                stage-2 rows2*(H + H/128*4) + metadata rows2*3*4 written
     combine  : rows2*H*2 read, weights n*K*4 + row map n*K*4 read,
                n*H*2 written
+    With the per-rank stage 2 a stage-2 row also carries the token's K local
+    expert ids and weights (+2K*4), and the combine reads no weights.
     """
     row = H + H // 128 * 4
     route = n_tok * E * 4 + n_tok * K * 4
+    meta2 = 3 + (2 * K if per_rank else 0)
     dispatch = (n_tok * H * 2 + 2 * n_tok * K * 4 + rows1 * row + rows1 * (2 + 2 * K) * 4
-                + rows2 * row + rows2 * 3 * 4)
-    combine = rows2 * H * 2 + 2 * n_tok * K * 4 + n_tok * H * 2
+                + rows2 * row + rows2 * meta2 * 4)
+    combine = rows2 * H * 2 + (1 if per_rank else 2) * n_tok * K * 4 + n_tok * H * 2
     # headline total = scores + tokens + topk + weights + stage rows/meta + combine
     total = n_tok * E * 4 + dispatch + combine
     return dict(route=route, dispatch=dispatch, combine=combine, total=total)
@@ -239,14 +242,14 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
     }
 
 
-def run_ht(args, ep):
+def run_ht(args, ep, per_rank=False):
     w = I.HT_PREFILL
     n_tok, E, K, H = w.num_tokens, w.num_experts, w.top_k, w.hidden
     log(f"[bench] building inputs: {n_tok} tokens, hidden {H}, {E} experts, top-{K}")
     scores = I.scores_for(w)
     x = I.tokens_for(w)
     weights = I.normal_weights(n_tok, K, w.seed)
-    Y = I.normal_bf16(n_tok * K, H, I.COMBINE.seed)
+    Y = I.normal_bf16(n_tok * K, H, I.COMBINE.seed)   # (per rank: the first rows2 are used)
 
     dev = torch.device("cuda")
     sets = []
@@ -260,8 +263,10 @@ def run_ht(args, ep):
 
     g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
                            max_nodes_per_token=4, hidden=H, max_tokens_per_rank=n_tok,
-                           num_src_ranks=1, payload="fp8", num_cus=args.num_cus)
+                           num_src_ranks=1, payload="fp8", num_cus=args.num_cus,
+                           ht_stage2="rank" if per_rank else "expert")
     stream = torch.cuda.current_stream()
+    w_comb = None if per_rank else w_d   # per-rank rows are the ranks' weighted sums
 
     def step(j, ev=None):
         s = sets[j % N_SETS]
@@ -276,7 +281,7 @@ def run_ht(args, ep):
         ep.ep_dispatch(h, s["x"], topk_weights=w_d)
         if ev is not None:
             ev[3].record(stream)
-        ep.ep_combine(h, Y_d, w_d, s["out"])
+        ep.ep_combine(h, Y_d, w_comb, s["out"])
         if ev is not None:
             ev[4].record(stream)
         ep.ep_destroy_handle(h)
@@ -287,15 +292,17 @@ def run_ht(args, ep):
     rows2 = ep.ep_handle_get_num_recv(h, -1)
     rows1 = int(ep.ep_handle_get_map(h, ep._abi.EP_MAP_HT_RANK_COUNT).sum().item())
     ep.ep_destroy_handle(h)
-    ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E)
+    ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank)
 
     mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
-    config = {"workload": "ht_prefill_4096_plus_combine", "tokens": n_tok, "hidden": H,
-              "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
-              "max_nodes_per_token": 4, "stage1_rows": rows1, "stage2_rows": rows2,
-              "algorithmic_bytes_per_step": ab["total"]}
-    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=True)
-    if not args.no_cpu_baseline:
+    config = {"workload": "ht_prefill_4096_per_rank_plus_combine" if per_rank else "ht_prefill_4096_plus_combine",
+              "tokens": n_tok, "hidden": H, "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
+              "max_nodes_per_token": 4, "stage2": "per_rank" if per_rank else "per_expert",
+              "stage1_rows": rows1, "stage2_rows": rows2, "algorithmic_bytes_per_step": ab["total"]}
+    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=not per_rank)
+    if per_rank:
+        result["dtype"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
+    if not args.no_cpu_baseline and not per_rank:
         log("[bench] timing the CPU oracle on the same workload")
         result["cpu_baseline"] = cpu_baseline(scores, x, weights, Y, n_tok)
     ep.ep_destroy_group(g)
@@ -458,12 +465,14 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
                          "eager: every step is enqueued from Python")
-    ap.add_argument("--workload", choices=["ht_prefill", "ll_decode", "ll_decode_1src", "ht_backward"],
+    ap.add_argument("--workload", choices=["ht_prefill", "ht_prefill_rank", "ll_decode", "ll_decode_1src",
+                                           "ht_backward"],
                     default="ht_prefill",
                     help="ht_prefill: 4096 tokens, HT dispatch + combine (the headline); "
                          "ll_decode: 64 sources x 128 tokens, staged LL dispatch + combine; "
                          "ll_decode_1src: one source's 128 tokens; "
-                         "ht_backward: the backward pass at the prefill shape on forward handles")
+                         "ht_backward: the backward pass at the prefill shape on forward handles; "
+                         "ht_prefill_rank: the prefill step with the per-rank stage 2")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters), then exit")
@@ -488,8 +497,8 @@ def main(argv=None):
 
     import combine_ep_route_amd as ep
 
-    if args.workload == "ht_prefill":
-        result = run_ht(args, ep)
+    if args.workload in ("ht_prefill", "ht_prefill_rank"):
+        result = run_ht(args, ep, per_rank=args.workload == "ht_prefill_rank")
     elif args.workload == "ht_backward":
         result = run_ht_backward(args, ep)
     else:

@@ -21,6 +21,8 @@ EP_ERR_UNSUPPORTED = 5
 
 EP_MODE_LL = 0
 EP_MODE_HT = 1
+EP_HT_STAGE2_PER_EXPERT = 0
+EP_HT_STAGE2_PER_RANK = 1
 
 EP_DTYPE_F32 = 0
 EP_DTYPE_BF16 = 1
@@ -61,6 +63,8 @@ EP_BUF_HT_STAGE2 = 6
 EP_BUF_HT_STAGE2_SRC = 7
 EP_BUF_HT_STAGE2_TOKEN = 8
 EP_BUF_HT_STAGE2_K = 9
+EP_BUF_HT_STAGE2_TOPK = 10
+EP_BUF_HT_STAGE2_WEIGHTS = 11
 
 
 class EpTensor(ctypes.Structure):
@@ -93,6 +97,7 @@ class EpConfig(ctypes.Structure):
         ("max_handles", ctypes.c_int32),
         ("num_cus", ctypes.c_int32),
         ("ll_buffers", ctypes.c_int32),
+        ("ht_stage2", ctypes.c_int32),
         ("alloc_fn", ALLOC_FN),
         ("free_fn", FREE_FN),
         ("alloc_ctx", ctypes.c_void_p),

@@ -224,13 +224,19 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
       if (mok[k]) my_nodes |= 1ull << (me[k] / p.P);
+    // An entry without a stage-2 row of its own (invalid, or with the
+    // per-rank stage 2 not the token's first entry on its rank) has rank -1.
     int pos[KMAX];
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       pos[k] = -1;
       if (mok[k] && k < K) {
-        const int pre = p.hist_e[static_cast<int64_t>(j) * E + me[k]] + p.rank_e[i * K + k];
-        pos[k] = HT ? pre : (me[k] * p.S + s) * p.slots + pre;
+        const int re = p.rank_e[i * K + k];
+        if (re >= 0) {
+          const int key = (HT && p.s2_rank) ? me[k] / p.L : me[k];
+          const int pre = p.hist_e[static_cast<int64_t>(j) * p.E2 + key] + re;
+          pos[k] = HT ? pre : (me[k] * p.S + s) * p.slots + pre;
+        }
       }
     }
     // Stage-1 row of destination node n (uniform), or -1.
@@ -296,6 +302,18 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
             p.m2_src[r] = s;
             p.m2_tok[r] = t;
             p.m2_k[r] = k;
+          }
+          if (p.s2_rank && r >= 0 && lane < K) {
+            // the token's entries on this row's rank, as local expert ids
+            const int rk = me[k] / p.L;
+            int ev = -1;
+            bool okv = false;
+#pragma unroll
+            for (int q = 0; q < KMAX; ++q)
+              if (q == lane) { ev = me[q]; okv = mok[q]; }
+            const bool here = okv && ev / p.L == rk;
+            p.m2_topk[static_cast<int64_t>(r) * K + lane] = here ? ev - rk * p.L : -1;
+            p.m2_w[static_cast<int64_t>(r) * K + lane] = (here && p.w) ? p.w[i * K + lane] : 0.0f;
           }
         }
       } else if (!line_tail) {

@@ -58,6 +58,8 @@ struct Group {
   int64_t n_max = 0;       // S * T_max
   int64_t rows1_max = 0;   // HT stage-1 rows, worst case
   int64_t rows2_max = 0;   // HT stage-2 rows, worst case (n_max * K)
+  int s2_rank = 0;         // HT stage 2 per (token, rank)
+  int E2 = 0;              // stage-2 keys: E, or R per rank
   int tiles_max = 0;       // layout tiles, worst case
 
   // Device buffers (owned).
@@ -76,6 +78,8 @@ struct Group {
   int32_t* m2_src = nullptr;
   int32_t* m2_tok = nullptr;
   int32_t* m2_k = nullptr;
+  int32_t* m2_topk = nullptr;   // per-rank stage 2 only
+  float* m2_w = nullptr;
   int32_t* err = nullptr;
 
   std::vector<Handle*> handles;
@@ -139,6 +143,9 @@ struct LayoutArgs {
   int S, T, K, E, N, G, P;
   int slots;             // LL slots per (expert, source)
   int ht;                // 1 = HT maps, 0 = LL maps
+  int E2;                // stage-2 keys: E, or R with the per-rank stage 2
+  int L;                 // experts per rank
+  int s2_rank;           // HT stage 2 per (token, rank): key = e / L, first entry only
   int tps, n_tiles;
   int32_t* hist_e;
   int32_t* hist_n;
@@ -157,7 +164,8 @@ struct LayoutArgs {
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 
-// LDS bytes the HT prefix-scan workgroup needs for S sources of tps tiles.
+// LDS bytes the HT prefix-scan workgroup needs for S sources of tps tiles
+// (E = the stage-2 key count).
 size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps);
 
 // Receive stage of a dispatch: copy the [E, S] counters to out, or with
@@ -178,6 +186,7 @@ struct DispatchArgs {
   int out_fp8;            // payload is FP8
   int64_t n;
   int T, K, N, H, E, S, P, slots, tps;
+  int E2, L, s2_rank;     // stage-2 keys (E, or R per rank), experts per rank, per-rank flag
   int64_t row_bytes, msg_bytes;
   int64_t row_pitch, msg_pitch;   // strides of HT rows / LL messages in the buffers
   int ht;
@@ -205,6 +214,8 @@ struct DispatchArgs {
   int32_t* m2_src;
   int32_t* m2_tok;
   int32_t* m2_k;
+  int32_t* m2_topk;       // per-rank stage 2: the token's entries on the row's rank
+  float* m2_w;
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 

@@ -122,9 +122,9 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   extern __shared__ uint64_t masks[];
   const int nw = blockDim.x >> 6;
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-  const int E = a.E, N = a.N, K = a.K;
-  uint64_t* m_e = masks;              // [nw][E]
-  uint64_t* m_n = masks + nw * E;     // [nw][N]
+  const int E = a.E, N = a.N, K = a.K, E2 = a.E2;
+  uint64_t* m_e = masks;              // [nw][E2] stage-2 keys (experts, or ranks)
+  uint64_t* m_n = masks + nw * E2;    // [nw][N]
 
   const int j = blockIdx.x * nw + w;
   const bool tile_ok = j < a.n_tiles;
@@ -133,9 +133,24 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   const bool active = tile_ok && t < a.T;
   const int64_t i = static_cast<int64_t>(s) * a.T + t;
 
-  for (int x = tid; x < nw * (E + N); x += blockDim.x) masks[x] = 0;
+  for (int x = tid; x < nw * (E2 + N); x += blockDim.x) masks[x] = 0;
   Entries<KMAX> en;
   en.load(a.topk + (active ? i : 0) * K, K, E, active);
+  // Stage-2 key of each valid entry: its expert, or with the per-rank stage
+  // 2 its rank, carried only by the token's first entry on that rank.
+  int key[KMAX];
+  bool first[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    key[k] = a.s2_rank ? en.e[k] / a.L : en.e[k];
+    first[k] = en.ok[k];
+  }
+  if (a.s2_rank) {
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k)
+#pragma unroll
+      for (int q = 0; q < k; ++q) first[k] = first[k] && !(en.ok[q] && key[q] == key[k]);
+  }
   __syncthreads();
   const uint64_t bit = 1ull << lane;
   uint64_t nodes = 0;
@@ -147,7 +162,7 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       if (!en.ok[k]) continue;
-      atomicOr(reinterpret_cast<unsigned long long*>(&m_e[w * E + en.e[k]]), bit);
+      if (first[k]) atomicOr(reinterpret_cast<unsigned long long*>(&m_e[w * E2 + key[k]]), bit);
       nodes |= 1ull << (en.e[k] / a.P);
     }
     if (a.ht)
@@ -156,7 +171,7 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   }
   __syncthreads();
   if (tile_ok) {
-    for (int e = lane; e < E; e += 64) a.hist_e[static_cast<int64_t>(j) * E + e] = __popcll(m_e[w * E + e]);
+    for (int e = lane; e < E2; e += 64) a.hist_e[static_cast<int64_t>(j) * E2 + e] = __popcll(m_e[w * E2 + e]);
     if (a.ht)
       for (int n = lane; n < N; n += 64) a.hist_n[static_cast<int64_t>(j) * N + n] = __popcll(m_n[w * N + n]);
   }
@@ -164,7 +179,7 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
     const uint64_t below = bit - 1;
 #pragma unroll
     for (int k = 0; k < KMAX; ++k)
-      if (k < K) a.rank_e[i * K + k] = en.ok[k] ? __popcll(m_e[w * E + en.e[k]] & below) : -1;
+      if (k < K) a.rank_e[i * K + k] = first[k] ? __popcll(m_e[w * E2 + key[k]] & below) : -1;
     if (a.ht)
       for (int n = 0; n < N; ++n)
         a.rank_n[i * N + n] = ((nodes >> n) & 1) ? __popcll(m_n[w * N + n] & below) : -1;
@@ -177,7 +192,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
   extern __shared__ int smem[];
   const int B = blockDim.x;
   const int tid = threadIdx.x;
-  const int E = a.E, N = a.N;
+  const int E = a.E2, N = a.N;   // stage-2 keys: the experts, or the ranks (per-rank HT)
   const int n_tiles = a.n_tiles;
   if (!a.ht) {
     // LL: per (expert, source), prefix over the source's own tiles.
@@ -188,7 +203,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
           chunk_prefix(a.hist_e, 0, tps, 0, [=](int tt) { return static_cast<int64_t>(src * tps + tt) * E + e; });
     }
   } else {
-    // HT.  Keys: the E experts (sequence: every tile in order) and the R
+    // HT.  Keys: the E stage-2 keys (sequence: every tile in order) and the R
     // stage-1 ranks d = n*G + g (sequence: the tiles of the sources at
     // position g, tps consecutive tiles per source).  A thread owns one
     // (key, chunk) of each kind; it walks its chunk with pointer strides
@@ -363,10 +378,10 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((a.n_tiles + kCountWaves - 1) / kCountWaves)), block(kCountWaves * 64);
-  const size_t lds = count_lds_bytes(a.E, a.N);
+  const size_t lds = count_lds_bytes(a.E2, a.N);
   if (a.K <= 8) layout_count_kernel<8><<<grid, block, lds, stream>>>(a);
   else layout_count_kernel<32><<<grid, block, lds, stream>>>(a);
-  layout_scan_kernel<<<dim3(1), dim3(kScanThreads), a.ht ? layout_scan_lds_bytes(a.E, a.N, a.G, a.S, a.tps) : 0, stream>>>(a);
+  layout_scan_kernel<<<dim3(1), dim3(kScanThreads), a.ht ? layout_scan_lds_bytes(a.E2, a.N, a.G, a.S, a.tps) : 0, stream>>>(a);
   return hipGetLastError();
 }
 

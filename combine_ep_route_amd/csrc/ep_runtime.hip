@@ -172,6 +172,9 @@ DispatchArgs dispatch_base(const Handle* h) {
   p.E = g->cfg.num_experts;
   p.S = g->cfg.num_src_ranks;
   p.P = g->P;
+  p.E2 = g->E2;
+  p.L = g->L;
+  p.s2_rank = g->s2_rank;
   p.slots = g->cfg.max_tokens_per_rank;
   p.tps = h->tps;
   p.row_bytes = g->row_bytes;
@@ -242,7 +245,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   if (cfg.num_nodes <= 0 || cfg.ranks_per_node <= 0 || cfg.num_experts <= 0 || cfg.top_k <= 0 ||
       cfg.hidden <= 0 || cfg.max_tokens_per_rank <= 0 || cfg.num_src_ranks <= 0 ||
       cfg.max_nodes_per_token < 0 || cfg.max_handles < 0 || cfg.num_cus < 0 || cfg.ll_buffers < 0 ||
-      cfg.ll_buffers > 2)
+      cfg.ll_buffers > 2 || (cfg.ht_stage2 != EP_HT_STAGE2_PER_EXPERT && cfg.ht_stage2 != EP_HT_STAGE2_PER_RANK))
     return EP_ERR_INVALID_ARGUMENT;
   const int64_t R = static_cast<int64_t>(cfg.num_nodes) * cfg.ranks_per_node;
   if (cfg.num_experts % R != 0) return EP_ERR_INVALID_ARGUMENT;
@@ -260,8 +263,10 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   if (cfg.num_src_ranks > R) return EP_ERR_UNSUPPORTED;
   if (E > kMaxExperts || K > kMaxTopK || N > kMaxNodes || R > kMaxRanks || cfg.hidden > kMaxHidden)
     return EP_ERR_UNSUPPORTED;
+  const bool s2_rank = cfg.mode == EP_MODE_HT && cfg.ht_stage2 == EP_HT_STAGE2_PER_RANK;
+  const int E2 = s2_rank ? static_cast<int>(R) : E;
   if (cfg.mode == EP_MODE_HT &&
-      layout_scan_lds_bytes(E, N, cfg.ranks_per_node, cfg.num_src_ranks,
+      layout_scan_lds_bytes(E2, N, cfg.ranks_per_node, cfg.num_src_ranks,
                             (cfg.max_tokens_per_rank + kLayoutTile - 1) / kLayoutTile) > 65536)
     return EP_ERR_UNSUPPORTED;   // more tiles than one workgroup's prefix scan holds
   if (cfg.max_handles == 0) cfg.max_handles = 2;
@@ -277,6 +282,8 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   g->M = M;
   g->J = J;
   g->fp8 = cfg.payload == EP_DTYPE_FP8_E4M3;
+  g->s2_rank = s2_rank;
+  g->E2 = E2;
   g->row_bytes = g->fp8 ? cfg.hidden + cfg.hidden / 128 * 4 : static_cast<int64_t>(cfg.hidden) * 2;
   g->msg_bytes = g->row_bytes + 16;
   g->row_pitch = (g->row_bytes + 127) / 128 * 128;
@@ -314,12 +321,17 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
       g->st2 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows2_max * g->row_pitch), &st));
     if (st == EP_OK) {
       const size_t r2 = static_cast<size_t>(g->rows2_max);
-      uint8_t* b = static_cast<uint8_t*>(dev_alloc(g, align_up(r2 * 4) * 3, &st));
+      const size_t extra = s2_rank ? align_up(r2 * K * 4) * 2 : 0;   // received top-k and weights
+      uint8_t* b = static_cast<uint8_t*>(dev_alloc(g, align_up(r2 * 4) * 3 + extra, &st));
       if (b) {
         Carve cv{b};
         g->m2_src = cv.take<int32_t>(r2);
         g->m2_tok = cv.take<int32_t>(r2);
         g->m2_k = cv.take<int32_t>(r2);
+        if (s2_rank) {
+          g->m2_topk = cv.take<int32_t>(r2 * K);
+          g->m2_w = cv.take<float>(r2 * K);
+        }
       }
     }
   }
@@ -475,6 +487,9 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.P = g->P;
   a.slots = g->cfg.max_tokens_per_rank;
   a.ht = g->cfg.mode == EP_MODE_HT;
+  a.E2 = g->E2;
+  a.L = g->L;
+  a.s2_rank = g->s2_rank;
   a.tps = h->tps;
   a.n_tiles = h->n_tiles;
   a.hist_e = h->hist_e;
@@ -498,8 +513,8 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
     // Nothing routed: counts and offsets are zero.
     EP_HIP(launch_fill_i32(h->c1, g->R, 0, s));
     EP_HIP(launch_fill_i32(h->off1, g->R, 0, s));
-    EP_HIP(launch_fill_i32(h->c2, a.E, 0, s));
-    EP_HIP(launch_fill_i32(h->off2, a.E, 0, s));
+    EP_HIP(launch_fill_i32(h->c2, a.E2, 0, s));
+    EP_HIP(launch_fill_i32(h->off2, a.E2, 0, s));
   } else if (n == 0) {
     EP_HIP(launch_fill_i32(h->ll_count, static_cast<int64_t>(a.E) * S, 0, s));
   }
@@ -526,12 +541,15 @@ EP_API ep_status_t ep_handle_get_num_recv(ep_handle_t handle, int32_t rank, int6
   if (rank < -1 || rank >= g->R) return EP_ERR_INVALID_ARGUMENT;
   const int E = g->cfg.num_experts, S = g->cfg.num_src_ranks, L = g->L;
   const bool ll = g->cfg.mode == EP_MODE_LL;
-  const size_t count = ll ? static_cast<size_t>(E) * S : static_cast<size_t>(E);
+  const size_t count = ll ? static_cast<size_t>(E) * S : static_cast<size_t>(g->E2);
   std::vector<int32_t> host(count);
   EP_HIP(hipStreamSynchronize(h->stream));
   EP_HIP(hipMemcpy(host.data(), ll ? h->ll_count : h->c2, count * sizeof(int32_t), hipMemcpyDeviceToHost));
   int64_t total = 0;
-  const int e0 = rank < 0 ? 0 : rank * L, e1 = rank < 0 ? E : (rank + 1) * L;
+  // The rank's keys: its experts, or with the per-rank stage 2 the rank itself.
+  const int keys = ll ? E : g->E2;
+  const int per = g->s2_rank ? 1 : L;
+  const int e0 = rank < 0 ? 0 : rank * per, e1 = rank < 0 ? keys : (rank + 1) * per;
   for (int e = e0; e < e1; ++e) {
     if (ll) for (int s = 0; s < S; ++s) total += host[static_cast<size_t>(e) * S + s];
     else total += host[e];
@@ -556,8 +574,8 @@ EP_API ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tenso
     case EP_MAP_HT_ROW: if (ll) break; fill_view(view, h->row2, EP_DTYPE_I32, h->n, K, EP_TAG_NONE); return EP_OK;
     case EP_MAP_HT_RANK_COUNT: if (ll) break; fill_view(view, h->c1, EP_DTYPE_I32, g->R, 0, EP_TAG_NONE); return EP_OK;
     case EP_MAP_HT_RANK_OFFSET: if (ll) break; fill_view(view, h->off1, EP_DTYPE_I32, g->R, 0, EP_TAG_NONE); return EP_OK;
-    case EP_MAP_HT_EXPERT_COUNT: if (ll) break; fill_view(view, h->c2, EP_DTYPE_I32, E, 0, EP_TAG_TOKENS_PER_EXPERT); return EP_OK;
-    case EP_MAP_HT_EXPERT_OFFSET: if (ll) break; fill_view(view, h->off2, EP_DTYPE_I32, E, 0, EP_TAG_NONE); return EP_OK;
+    case EP_MAP_HT_EXPERT_COUNT: if (ll) break; fill_view(view, h->c2, EP_DTYPE_I32, g->E2, 0, EP_TAG_TOKENS_PER_EXPERT); return EP_OK;
+    case EP_MAP_HT_EXPERT_OFFSET: if (ll) break; fill_view(view, h->off2, EP_DTYPE_I32, g->E2, 0, EP_TAG_NONE); return EP_OK;
     default: break;
   }
   return EP_ERR_INVALID_ARGUMENT;
@@ -590,7 +608,7 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   int per_expert = 0;
   if (recv_counts) {
     const bool one_d = recv_counts->dtype == EP_DTYPE_I32 && recv_counts->ndim == 1 &&
-                       recv_counts->sizes[0] == E && recv_counts->strides[0] == 1 && recv_counts->data &&
+                       recv_counts->sizes[0] == (ll ? E : g->E2) && recv_counts->strides[0] == 1 && recv_counts->data &&
                        (recv_counts->tag == EP_TAG_NONE || recv_counts->tag == EP_TAG_TOKENS_PER_EXPERT);
     const bool two_d = ll && recv_counts->ndim == 2 &&
                        check2d(recv_counts, EP_DTYPE_I32, E, S, EP_TAG_TOKENS_PER_EXPERT, false) &&
@@ -629,6 +647,8 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   p.m2_src = g->m2_src;
   p.m2_tok = g->m2_tok;
   p.m2_k = g->m2_k;
+  p.m2_topk = g->m2_topk;
+  p.m2_w = g->m2_w;
   if (const ep_status_t st = from_hip(launch_dispatch(p, s)); st != EP_OK) return st;
   h->maps_ready = true;
   if (ll) {
@@ -645,7 +665,7 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   }
   if (counts_out)
     return from_hip(ll ? launch_recv_counts(h->ll_count, E, S, per_expert, counts_out, s)
-                       : launch_recv_counts(h->c2, E, 1, 0, counts_out, s));
+                       : launch_recv_counts(h->c2, g->E2, 1, 0, counts_out, s));
   return EP_OK;
 }
 
@@ -666,6 +686,8 @@ ep_status_t buffer_view(Group* g, int32_t which, int ll_half, ep_tensor_t* view)
     case EP_BUF_HT_STAGE2_SRC: if (ll) break; fill_view(view, g->m2_src, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE2_TOKEN: if (ll) break; fill_view(view, g->m2_tok, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
     case EP_BUF_HT_STAGE2_K: if (ll) break; fill_view(view, g->m2_k, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
+    case EP_BUF_HT_STAGE2_TOPK: if (!g->s2_rank) break; fill_view(view, g->m2_topk, EP_DTYPE_I32, g->rows2_max, K, EP_TAG_TOPK_IDX); return EP_OK;
+    case EP_BUF_HT_STAGE2_WEIGHTS: if (!g->s2_rank) break; fill_view(view, g->m2_w, EP_DTYPE_F32, g->rows2_max, K, EP_TAG_TOPK_WEIGHTS); return EP_OK;
     default: break;
   }
   return EP_ERR_INVALID_ARGUMENT;
@@ -700,8 +722,10 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
   const bool ll = g->cfg.mode == EP_MODE_LL;
   ep_tensor_t y2;
   if (!expert_rows(g, expert_out, &y2)) return EP_ERR_INVALID_ARGUMENT;
-  if (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) || !contiguous2d(topk_weights))
+  if (topk_weights && (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) ||
+                       !contiguous2d(topk_weights)))
     return EP_ERR_INVALID_ARGUMENT;
+  if (g->s2_rank && topk_weights) return EP_ERR_INVALID_ARGUMENT;   // rank rows are weighted already
   if (!check2d(out, EP_DTYPE_BF16, h->n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
   if (send_only && !ll) return EP_ERR_UNSUPPORTED;
   if (h->pend != Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;   // complete the staged one first
@@ -713,7 +737,7 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
   a.y = static_cast<const uint16_t*>(y2.data);
   a.ld_y = y2.strides[0];
   a.rows = y2.sizes[0];
-  a.w = static_cast<const float*>(topk_weights->data);
+  a.w = topk_weights ? static_cast<const float*>(topk_weights->data) : nullptr;   // null: unit weights
   a.loc = ll ? h->slot_map : h->row2;
   a.n = h->n;
   a.K = K;
@@ -744,6 +768,7 @@ EP_API ep_status_t ep_combine_backward(ep_handle_t handle, const ep_tensor_t* gr
   Group* g = h->g;
   const int H = g->cfg.hidden, K = g->cfg.top_k;
   const bool ll = g->cfg.mode == EP_MODE_LL;
+  if (g->s2_rank) return EP_ERR_UNSUPPORTED;   // the experts apply the weights: nothing to differentiate here
   if (!check2d(grad_out, EP_DTYPE_BF16, h->n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
   if (!check2d(topk_weights, EP_DTYPE_F32, h->n, K, EP_TAG_TOPK_WEIGHTS, false) || !contiguous2d(topk_weights))
     return EP_ERR_INVALID_ARGUMENT;

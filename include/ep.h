@@ -56,6 +56,15 @@ typedef enum {
  * config selects HT or LL). */
 typedef enum { EP_MODE_LL = 0, EP_MODE_HT = 1 } ep_mode_t;
 
+/* HT stage-2 layout ("NVSHMEM and DeepEP", high-throughput mode: the
+ * traffic study compares one copy per expert with one per destination GPU).
+ *   PER_EXPERT: one row per valid (token, k), grouped by expert.
+ *   PER_RANK:   one row per (token, distinct destination rank), grouped by
+ *               rank, with the token's entries local to that rank (DeepEP's
+ *               received top-k form); the experts' weighted partial sums come
+ *               back per rank and the combine sums them. */
+typedef enum { EP_HT_STAGE2_PER_EXPERT = 0, EP_HT_STAGE2_PER_RANK = 1 } ep_ht_stage2_t;
+
 /* Element types (NCCL-EP tensor abstraction: FP32/BF16/FP16/FP8). */
 typedef enum {
     EP_DTYPE_F32 = 0,
@@ -124,6 +133,7 @@ typedef struct {
     int32_t num_cus;             /* cap on CUs used by dispatch/combine; 0=all */
     int32_t ll_buffers;          /* LL receive buffers used in turn: 1 or 2;
                                     0 means 2 (double buffering, NCCL-EP LL) */
+    int32_t ht_stage2;           /* ep_ht_stage2_t (HT only)                   */
     /* Optional allocator hooks: both or neither.  alloc_fn returns device
      * memory of at least `bytes` bytes aligned to 256, or NULL. */
     void *(*alloc_fn)(size_t bytes, void *ctx);
@@ -216,11 +226,14 @@ typedef enum {
     EP_MAP_LL_SLOT = 0,   /* I32 [n, K]: global slot (e*S+s)*T_max + slot, or -1 */
     EP_MAP_LL_COUNT = 1,  /* I32 [E, S]                                          */
     EP_MAP_HT_NODE_ROW = 2, /* I32 [n, N]: global stage-1 row, or -1            */
-    EP_MAP_HT_ROW = 3,    /* I32 [n, K]: global stage-2 row, or -1               */
+    EP_MAP_HT_ROW = 3,    /* I32 [n, K]: global stage-2 row, or -1.  PER_RANK: the
+                             row of the entry's rank at the token's first entry
+                             on that rank, -1 at its other entries            */
     EP_MAP_HT_RANK_COUNT = 4,  /* I32 [R]: stage-1 rows per destination rank    */
     EP_MAP_HT_RANK_OFFSET = 5, /* I32 [R]: exclusive prefix sum of the above    */
-    EP_MAP_HT_EXPERT_COUNT = 6,  /* I32 [E]: stage-2 rows per expert            */
-    EP_MAP_HT_EXPERT_OFFSET = 7  /* I32 [E]: exclusive prefix sum of the above  */
+    EP_MAP_HT_EXPERT_COUNT = 6,  /* I32 [E]: stage-2 rows per expert
+                                    (PER_RANK: [R] rows per rank)             */
+    EP_MAP_HT_EXPERT_OFFSET = 7  /* exclusive prefix sum of the above          */
 } ep_map_t;
 ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *view);
 
@@ -250,7 +263,7 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  *            metadata.  Ignored in LL.
  *   recv_counts  : optional I32 out, tag TOKENS_PER_EXPERT: LL [E, S]
  *            counts per (expert, source) or [E] tokens per expert; HT [E]
- *            stage-2 rows per expert.
+ *            stage-2 rows per expert (PER_RANK: [R] rows per rank).
  *   send_only : 0, or (LL) enqueue the send stage only; HT returns
  *            EP_ERR_UNSUPPORTED (the staged mode is an LL feature).
  * With an FP8 payload each 128-element block is quantised as
@@ -287,7 +300,10 @@ typedef enum {
     EP_BUF_HT_STAGE2 = 6,      /* U8 [S*T_max*K, row]                         */
     EP_BUF_HT_STAGE2_SRC = 7,    /* I32 [S*T_max*K]                           */
     EP_BUF_HT_STAGE2_TOKEN = 8,  /* I32 [S*T_max*K]                           */
-    EP_BUF_HT_STAGE2_K = 9       /* I32 [S*T_max*K]                           */
+    EP_BUF_HT_STAGE2_K = 9,      /* I32 [S*T_max*K]: k of the row's (first) entry */
+    EP_BUF_HT_STAGE2_TOPK = 10,  /* PER_RANK: I32 [S*T_max*K, K] the token's entries
+                                    on the row's rank as local expert ids, else -1 */
+    EP_BUF_HT_STAGE2_WEIGHTS = 11 /* PER_RANK: F32 [S*T_max*K, K] their weights, else 0 */
 } ep_buffer_t;
 ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
 
@@ -309,7 +325,11 @@ ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t 
  *   expert_out   : BF16 [rows, H] (or [E, S*T_max, H] in LL), innermost
  *                  contiguous, rows 16-byte aligned.  A row index >= rows
  *                  sets EP_DEVERR_ROW_RANGE and is skipped.
- *   topk_weights : F32 [n, K] contiguous.
+ *   topk_weights : F32 [n, K] contiguous, or NULL for unit weights.  With
+ *                  the PER_RANK stage 2 the rows are the ranks' weighted
+ *                  partial sums: weights must be NULL, and the combine sums
+ *                  the token's rank rows in the order of the entries that
+ *                  name them.
  *   out          : BF16 [n, H], innermost contiguous, rows 16-byte aligned.
  *   send_only    : 0, or (LL) NCCL-EP's staged mode: the combine's receive
  *                  stage (the gather-reduce into out) is enqueued by
@@ -355,7 +375,9 @@ ep_status_t ep_complete(ep_handle_t handle, ep_stream_t stream);
  *   topk_weights    : F32 [n, K] contiguous.
  *   grad_expert_out : BF16 rows at the dispatch geometry ([rows, H], or LL
  *                     [E, S*T_max, H]).
- *   grad_weights    : optional F32 [n, K] contiguous. */
+ *   grad_weights    : optional F32 [n, K] contiguous.
+ * EP_ERR_UNSUPPORTED with the PER_RANK stage 2 (the experts apply the
+ * weights there, so the combine has none to differentiate). */
 ep_status_t ep_combine_backward(ep_handle_t handle, const ep_tensor_t *grad_out,
                                 const ep_tensor_t *expert_out,
                                 const ep_tensor_t *topk_weights,

@@ -97,7 +97,7 @@ def _create(cfg):
     dict(mode=7), dict(num_nodes=0), dict(num_experts=100), dict(top_k=0),
     dict(top_k=300), dict(hidden=7000), dict(hidden=200), dict(payload=A.EP_DTYPE_F32),
     dict(max_tokens_per_rank=0), dict(num_src_ranks=0), dict(max_nodes_per_token=-1),
-    dict(ll_buffers=-1), dict(ll_buffers=3),
+    dict(ll_buffers=-1), dict(ll_buffers=3), dict(ht_stage2=2), dict(ht_stage2=-1),
     dict(max_nodes_per_token=1, top_k=40),          # 1 node x 32 experts < 40
     dict(num_experts=64, max_nodes_per_token=1, top_k=16),  # ceil(16/1)=16 > 8 per node
 ])
@@ -174,6 +174,24 @@ def test_ll_double_buffering_memory():
     one_buffer = 256 * 4 * 32 * 7424          # messages at their 128-byte pitch
     assert sizes[0] == sizes[2]
     assert sizes[2] - sizes[1] == one_buffer
+
+
+def test_per_rank_stage2_memory():
+    # the per-rank stage 2 adds the received top-k ids and weights per row
+    sizes = {}
+    for mode in (A.EP_HT_STAGE2_PER_EXPERT, A.EP_HT_STAGE2_PER_RANK):
+        pool = HostPool()
+        st, g = _create(_cfg(pool, ht_stage2=mode, max_tokens_per_rank=256))
+        assert st == A.EP_OK
+        b = ctypes.c_int64()
+        assert A.lib().ep_group_memory(g, ctypes.byref(b)) == A.EP_OK
+        sizes[mode] = b.value
+        view = A.EpTensor()
+        want = A.EP_OK if mode == A.EP_HT_STAGE2_PER_RANK else A.EP_ERR_INVALID_ARGUMENT
+        assert A.lib().ep_get_buffer(g, A.EP_BUF_HT_STAGE2_TOPK, ctypes.byref(view)) == want
+        A.lib().ep_destroy_group(g)
+    rows2 = 256 * 8
+    assert sizes[A.EP_HT_STAGE2_PER_RANK] - sizes[A.EP_HT_STAGE2_PER_EXPERT] >= 2 * rows2 * 8 * 4
 
 
 def test_staged_calls_reject_null_handles():
