@@ -20,9 +20,16 @@ namespace {
 
 constexpr int kTokensPerBlock = 4;
 
-__device__ __forceinline__ uint32_t ordered_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// 64-bit selection key of (score f, expert e): the score's bits in unsigned
+// order (-0 taken as +0 and a NaN below every number, as a float comparison
+// has them), then the complemented index, so that a larger key is a higher
+// score or, at equal scores, a lower index.  Key 0 is below every expert.
+__device__ __forceinline__ uint64_t select_key(float f, int e) {
+  const float c = f + 0.0f;   // -0 -> +0
+  const uint32_t u = __float_as_uint(c);
+  uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if (c != c) o = 0;
+  return (static_cast<uint64_t>(o) << 32) | (0xFFFFFFFFu - static_cast<uint32_t>(e));
 }
 
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
@@ -96,8 +103,7 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
   for (int v = 0; v < NV; ++v) {
     const int e = v * 64 + lane;
     const bool ok = e < E && (!limited || s_keep[wave][e / P]);
-    key[v] = ok ? ((static_cast<uint64_t>(ordered_bits(val[v])) << 32) |
-                   (0xFFFFFFFFu - static_cast<uint32_t>(e)))
+    key[v] = ok ? select_key(val[v], e)
                 : 0ull;
   }
 
@@ -123,7 +129,10 @@ __global__ __launch_bounds__(256) void route_kernel(RouteArgs a) {
 // experts per lane (one or more 16-byte loads), a node spans LPN = P/V lanes
 // (a power of two).  All cross-lane steps are DPP row permutations or
 // ds_swizzle inside the 32-lane half, so nothing waits on LDS except the
-// single exchange of the N node scores.
+// single exchange of the N node scores.  The K experts come from a merge
+// tree (each lane sorts its V selection keys, five pairwise merges over the
+// exchange pattern leave the V best in every lane) when K <= V and V is a
+// power of two, else from K rounds of a 32-lane maximum.
 // ---------------------------------------------------------------------------
 
 constexpr int kFastTokensPerBlock = 8;   // 4 waves x 2 tokens
@@ -151,16 +160,67 @@ __device__ __forceinline__ int xchg(int x) {
 template <int STEP>
 __device__ __forceinline__ float xchgf(float x) { return __int_as_float(xchg<STEP>(__float_as_int(x))); }
 
-// (v, i) beats (w, j) when v > w, or v == w and i < j.
-__device__ __forceinline__ bool beats(float v, int i, float w, int j) {
-  return v > w || (v == w && i < j);
+
+// Compare-exchange of two keys so that a holds the larger.
+__device__ __forceinline__ void cx(uint64_t& a, uint64_t& b) {
+  const uint64_t x = a, y = b;
+  const bool sw = y > x;
+  a = sw ? y : x;
+  b = sw ? x : y;
 }
 
+// Sort V keys (a power of two) largest first: bitonic network.
+template <int V>
+__device__ __forceinline__ void bitonic_sort_desc(uint64_t (&k)[V]) {
+#pragma unroll
+  for (int size = 2; size <= V; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < V; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          if ((i & size) == 0) cx(k[i], k[j]);
+          else cx(k[j], k[i]);
+        }
+      }
+}
+
+// One level of the merge tree: the union of the lane's sorted V keys and its
+// partner's (exchange STEP) cut to its V largest, sorted.  max(mine[i],
+// partner[V-1-i]) is a bitonic sequence holding the V largest; a half-cleaner
+// cascade sorts it.  Both partners end with the same list.
+template <int STEP, int V>
+__device__ __forceinline__ void merge_level(uint64_t (&k)[V]) {
+  uint64_t o[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint32_t hi = static_cast<uint32_t>(xchg<STEP>(static_cast<int>(k[i] >> 32)));
+    const uint32_t lo = static_cast<uint32_t>(xchg<STEP>(static_cast<int>(k[i])));
+    o[i] = (static_cast<uint64_t>(hi) << 32) | lo;
+  }
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const uint64_t p = o[V - 1 - i];
+    k[i] = p > k[i] ? p : k[i];
+  }
+#pragma unroll
+  for (int stride = V >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      const int j = i ^ stride;
+      if (j > i) cx(k[i], k[j]);
+    }
+}
+
+// One exchange of a 32-lane maximum of 64-bit keys held as (hi, lo).
 template <int STEP>
-__device__ __forceinline__ void argmax_step(float& v, int& i) {
-  const float ov = xchgf<STEP>(v);
-  const int oi = xchg<STEP>(i);
-  if (beats(ov, oi, v, i)) { v = ov; i = oi; }
+__device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
+  const uint32_t ohi = static_cast<uint32_t>(xchg<STEP>(static_cast<int>(hi)));
+  const uint32_t olo = static_cast<uint32_t>(xchg<STEP>(static_cast<int>(lo)));
+  const uint64_t o = (static_cast<uint64_t>(ohi) << 32) | olo;
+  const uint64_t m = (static_cast<uint64_t>(hi) << 32) | lo;
+  if (o > m) { hi = ohi; lo = olo; }
 }
 
 // Merge the node top-2 (a1 >= a2) with a partner group's over one exchange.
@@ -222,27 +282,41 @@ __global__ __launch_bounds__(256) void route_fast_kernel(RouteArgs a) {
     keep = rank < a.M;
   }
 
-  // K rounds of a 32-lane arg-max over the remaining candidates.
   const int e0 = hl * V;
-  bool alive[V];
+  uint64_t key[V];
 #pragma unroll
-  for (int v = 0; v < V; ++v) alive[v] = keep;
+  for (int v = 0; v < V; ++v) key[v] = keep ? select_key(val[v], e0 + v) : 0ull;
   int mine = -1;
-  for (int k = 0; k < a.K; ++k) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+  if ((V & (V - 1)) == 0 && a.K <= V) {
+    // Merge tree: sort the lane's keys, then five levels of pairwise merges
+    // over the 32 lanes leave every lane with the token's V best, in order.
+    bitonic_sort_desc<V>(key);
+    merge_level<0, V>(key);
+    merge_level<1, V>(key);
+    merge_level<2, V>(key);
+    merge_level<3, V>(key);
+    merge_level<4, V>(key);
 #pragma unroll
     for (int v = 0; v < V; ++v)
-      if (alive[v] && beats(val[v], e0 + v, bv, bi)) { bv = val[v]; bi = e0 + v; }
-    argmax_step<0>(bv, bi);
-    argmax_step<1>(bv, bi);
-    argmax_step<2>(bv, bi);
-    argmax_step<3>(bv, bi);
-    argmax_step<4>(bv, bi);
-    if (hl == k) mine = bi;
+      if (hl == v) mine = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key[v]));
+  } else {
+    // K rounds of a 32-lane maximum of the lanes' best remaining keys.
+    for (int k = 0; k < a.K; ++k) {
+      uint64_t best = 0;
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (bi == e0 + v) alive[v] = false;
+      for (int v = 0; v < V; ++v) best = key[v] > best ? key[v] : best;
+      uint32_t hi = static_cast<uint32_t>(best >> 32), lo = static_cast<uint32_t>(best);
+      max_step<0>(hi, lo);
+      max_step<1>(hi, lo);
+      max_step<2>(hi, lo);
+      max_step<3>(hi, lo);
+      max_step<4>(hi, lo);
+      const uint64_t w = (static_cast<uint64_t>(hi) << 32) | lo;
+      if (hl == k) mine = static_cast<int>(0xFFFFFFFFu - lo);
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (key[v] == w) key[v] = 0;
+    }
   }
   if (active && hl < a.K) a.topk[t * a.K + hl] = mine;
 }

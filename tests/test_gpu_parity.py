@@ -60,6 +60,29 @@ def test_route_shapes_and_ties(E, N, G, K, M, n):
         ep.ep_destroy_group(g)
 
 
+@pytest.mark.parametrize("E,N,G,K,M", [(256, 8, 8, 8, 4), (96, 4, 2, 6, 2), (256, 8, 8, 8, 0)])
+def test_route_signed_zero_and_negative_ties(E, N, G, K, M):
+    """-0 and +0 are equal scores (ties go to the lower index), negative and
+    -inf scores order below them, on the fast (E % 128 == 0) and the generic
+    routing kernels."""
+    say(f"route signed-zero ties E={E} M={M}")
+    rng = np.random.default_rng(E + 17)
+    n = 300
+    scores = rng.choice(np.array([0.0, -0.0, 0.25, -0.25, -np.inf, 1.5], np.float32), size=(n, E))
+    scores[::4] = -0.0                              # all-zero rows: pure index order
+    scores[1::4, ::2] = 0.0
+    g = ep.ep_create_group(mode="ht", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=128, max_tokens_per_rank=n,
+                           num_src_ranks=1, payload="fp8")
+    try:
+        got = route_gpu(g, scores, K)
+        np.testing.assert_array_equal(got, oracle.route(scores, N, K, M))
+        if M == 0:
+            np.testing.assert_array_equal(got[0], np.arange(K))
+    finally:
+        ep.ep_destroy_group(g)
+
+
 def test_route_empty_and_strided():
     g = ep.ep_create_group(mode="ht", max_tokens_per_rank=64)
     try:
