@@ -49,54 +49,12 @@ struct Entries {
   }
 };
 
-// Exclusive scan of v[0..count) in place by the whole block.
-__device__ void block_exclusive_scan(int* v, int count, int* scratch) {
-  const int B = blockDim.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int per = (count + B - 1) / B;
-  const int x0 = tid * per;
-  int sum = 0;
-  for (int q = 0; q < per; ++q)
-    if (x0 + q < count) sum += v[x0 + q];
-  int incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  if (lane == 63) scratch[w] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int q = 0; q < w; ++q) base += scratch[q];
-  int run = base + incl - sum;
-  for (int q = 0; q < per; ++q) {
-    if (x0 + q < count) {
-      const int val = v[x0 + q];
-      v[x0 + q] = run;
-      run += val;
-    }
-  }
-  __syncthreads();
-}
-
 constexpr int kScanRegs = 16;      // tile counts a scan thread keeps in registers
 
-// Sum / exclusive-prefix rewrite of values at idx(pos), pos in [p0, p1),
-// 16 independent loads at a time so that the chain costs one round trip per
-// 16 tiles instead of one per tile.
+// Exclusive-prefix rewrite of values at idx(pos), pos in [p0, p1), 16
+// independent loads at a time so that the chain costs one round trip per 16
+// tiles instead of one per tile.
 constexpr int kBatch = 16;
-
-template <class Idx>
-__device__ __forceinline__ int chunk_sum(const int32_t* base, int p0, int p1, Idx idx) {
-  int sum = 0;
-  for (int pos = p0; pos < p1; pos += kBatch) {
-    int v[kBatch];
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) v[q] = pos + q < p1 ? base[idx(pos + q)] : 0;
-#pragma unroll
-    for (int q = 0; q < kBatch; ++q) sum += v[q];
-  }
-  return sum;
-}
 
 template <class Idx>
 __device__ __forceinline__ int chunk_prefix(int32_t* base, int p0, int p1, int run, Idx idx) {
@@ -210,16 +168,18 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     // (no divisions in the loops) and keeps up to kScanRegs counts in
     // registers between the sum and the rewrite.
     const int G = a.G, R = N * G, tps = a.tps;
-    const int ce = B / E > 0 ? B / E : 1;                 // expert chunks
-    const int cl_e = (n_tiles + ce - 1) / ce;             // tiles per expert chunk
-    const int cr = B / R > 0 ? B / R : 1;                 // rank chunks
+    // Chunks per key: enough for kScanRegs tiles each, at most B / keys.
     const int max_rail = ((a.S + G - 1) / G) * tps;
+    const int ce = max(1, min(B / E, (n_tiles + kScanRegs - 1) / kScanRegs));    // expert chunks
+    const int cl_e = (n_tiles + ce - 1) / ce;             // tiles per expert chunk
+    const int cr = max(1, min(B / R, (max_rail + kScanRegs - 1) / kScanRegs));   // rank chunks
     const int cl_r = (max_rail + cr - 1) / cr;            // tiles per rank chunk
     int* part_e = smem;                  // [ce][E]
     int* part_r = part_e + ce * E;       // [cr][R]
     int* tot_e = part_r + cr * R;        // [E]
     int* tot_r = tot_e + E;              // [R]
-    int* scratch = tot_r + R;            // [B/64]
+    int* scratch = tot_r + R;            // [2][B/64]
+    const int lane = tid & 63, wv = tid >> 6, nw = B >> 6;
 
     // Expert pair (e, c): tiles [c*cl_e, ...), address stride E.
     const bool has_e = tid < ce * E;
@@ -259,31 +219,45 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     if (has_e) part_e[ce_i * E + e] = se;
     if (has_r) part_r[cr_i * R + d] = sr;
     __syncthreads();
-    for (int x = tid; x < E; x += B) {
-      int run = 0;
+    // Thread x owns key x of each kind (E, R <= B): prefix over the key's
+    // chunks, then one exclusive scan of the key totals across the
+    // workgroup (shuffles inside a wave, one barrier across waves).
+    int te = 0, tr = 0;
+    if (tid < E) {
       for (int c = 0; c < ce; ++c) {
-        const int t = part_e[c * E + x];
-        part_e[c * E + x] = run;
-        run += t;
+        const int t = part_e[c * E + tid];
+        part_e[c * E + tid] = te;
+        te += t;
       }
-      tot_e[x] = run;
-      a.c2[x] = run;
+      a.c2[tid] = te;
     }
-    for (int x = tid; x < R; x += B) {
-      int run = 0;
+    if (tid < R) {
       for (int c = 0; c < cr; ++c) {
-        const int t = part_r[c * R + x];
-        part_r[c * R + x] = run;
-        run += t;
+        const int t = part_r[c * R + tid];
+        part_r[c * R + tid] = tr;
+        tr += t;
       }
-      tot_r[x] = run;
-      a.c1[x] = run;
+      a.c1[tid] = tr;
+    }
+    int ie = te, ir = tr;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int oe = __shfl_up(ie, off, 64), orr = __shfl_up(ir, off, 64);
+      if (lane >= off) { ie += oe; ir += orr; }
+    }
+    if (lane == 63) { scratch[wv] = ie; scratch[nw + wv] = ir; }
+    __syncthreads();
+    int be = 0, br = 0;
+    for (int q = 0; q < wv; ++q) { be += scratch[q]; br += scratch[nw + q]; }
+    if (tid < E) {
+      tot_e[tid] = be + ie - te;
+      a.off2[tid] = be + ie - te;
+    }
+    if (tid < R) {
+      tot_r[tid] = br + ir - tr;
+      a.off1[tid] = br + ir - tr;
     }
     __syncthreads();
-    block_exclusive_scan(tot_e, E, scratch);
-    block_exclusive_scan(tot_r, R, scratch);
-    for (int x = tid; x < E; x += B) a.off2[x] = tot_e[x];
-    for (int x = tid; x < R; x += B) a.off1[x] = tot_r[x];
     if (has_e) {
       int run = tot_e[e] + part_e[ce_i * E + e];
       if (regs) {
@@ -356,7 +330,7 @@ size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps) {
   const int R = N * G;
   const int ce = kScanThreads / E > 0 ? kScanThreads / E : 1;
   const int cr = kScanThreads / R > 0 ? kScanThreads / R : 1;
-  return (static_cast<size_t>(ce) * E + static_cast<size_t>(cr) * R + E + R + kScanThreads / 64) * 4;
+  return (static_cast<size_t>(ce) * E + static_cast<size_t>(cr) * R + E + R + 2 * (kScanThreads / 64)) * 4;
 }
 
 hipError_t launch_recv_counts(const int32_t* counts, int E, int S, int per_expert, int32_t* out,
