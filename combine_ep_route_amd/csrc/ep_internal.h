@@ -146,6 +146,7 @@ struct LayoutArgs {
   int E2;                // stage-2 keys: E, or R with the per-rank stage 2
   int L;                 // experts per rank
   int s2_rank;           // HT stage 2 per (token, rank): key = e / L, first entry only
+  int l_shift, p_shift;  // log2 of L and P when powers of two, else -1
   int tps, n_tiles;
   int32_t* hist_e;
   int32_t* hist_n;

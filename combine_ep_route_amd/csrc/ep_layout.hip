@@ -32,10 +32,24 @@ struct Entries {
   int bad = 0;
 
   // Loads K indices and flags the valid ones: in range and not a repeat of
-  // an earlier entry of the same token.
-  __device__ void load(const int32_t* row, int K, int E, bool active) {
+  // an earlier entry of the same token.  vec8: K == 8 and the row is 16-byte
+  // aligned, two 16-byte loads.
+  __device__ void load(const int32_t* row, int K, int E, bool active, bool vec8) {
+    if constexpr (KMAX == 8) {
+      if (vec8) {
+        const int4 m1{-1, -1, -1, -1};
+        const int4 lo = active ? reinterpret_cast<const int4*>(row)[0] : m1;
+        const int4 hi = active ? reinterpret_cast<const int4*>(row)[1] : m1;
+        e[0] = lo.x; e[1] = lo.y; e[2] = lo.z; e[3] = lo.w;
+        e[4] = hi.x; e[5] = hi.y; e[6] = hi.z; e[7] = hi.w;
+      } else {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) e[k] = (active && k < K) ? row[k] : -1;
+        for (int k = 0; k < KMAX; ++k) e[k] = (active && k < K) ? row[k] : -1;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k) e[k] = (active && k < K) ? row[k] : -1;
+    }
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       const bool in_range = e[k] >= 0 && e[k] < E;
@@ -92,15 +106,20 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   const int64_t i = static_cast<int64_t>(s) * a.T + t;
 
   for (int x = tid; x < nw * (E2 + N); x += blockDim.x) masks[x] = 0;
+  // Token rows of 8 entries, 16-byte aligned: vector loads and stores.
+  const bool vec8 = KMAX == 8 && K == 8 && (reinterpret_cast<uintptr_t>(a.topk) & 15u) == 0;
   Entries<KMAX> en;
-  en.load(a.topk + (active ? i : 0) * K, K, E, active);
+  en.load(a.topk + (active ? i : 0) * K, K, E, active, vec8);
+  // e / L and e / P by shifts when they are powers of two
+  auto div_l = [&](int e) { return a.l_shift >= 0 ? e >> a.l_shift : e / a.L; };
+  auto div_p = [&](int e) { return a.p_shift >= 0 ? e >> a.p_shift : e / a.P; };
   // Stage-2 key of each valid entry: its expert, or with the per-rank stage
   // 2 its rank, carried only by the token's first entry on that rank.
   int key[KMAX];
   bool first[KMAX];
 #pragma unroll
   for (int k = 0; k < KMAX; ++k) {
-    key[k] = a.s2_rank ? en.e[k] / a.L : en.e[k];
+    key[k] = a.s2_rank ? div_l(en.e[k]) : en.e[k];
     first[k] = en.ok[k];
   }
   if (a.s2_rank) {
@@ -113,15 +132,27 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   const uint64_t bit = 1ull << lane;
   uint64_t nodes = 0;
   if (active) {
+    if constexpr (KMAX == 8) {
+      if (vec8) {
+        int4* dst = reinterpret_cast<int4*>(a.topk_copy + i * 8);
+        dst[0] = int4{en.e[0], en.e[1], en.e[2], en.e[3]};
+        dst[1] = int4{en.e[4], en.e[5], en.e[6], en.e[7]};
+      } else {
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (k < K) a.topk_copy[i * K + k] = en.e[k];
+        for (int k = 0; k < KMAX; ++k)
+          if (k < K) a.topk_copy[i * K + k] = en.e[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (k < K) a.topk_copy[i * K + k] = en.e[k];
+    }
     if (en.bad) atomicOr(a.err, en.bad);
 #pragma unroll
     for (int k = 0; k < KMAX; ++k) {
       if (!en.ok[k]) continue;
       if (first[k]) atomicOr(reinterpret_cast<unsigned long long*>(&m_e[w * E2 + key[k]]), bit);
-      nodes |= 1ull << (en.e[k] / a.P);
+      nodes |= 1ull << div_p(en.e[k]);
     }
     if (a.ht)
       for (int n = 0; n < N; ++n)
@@ -135,12 +166,37 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   }
   if (active) {
     const uint64_t below = bit - 1;
+    int re[KMAX];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (k < K) a.rank_e[i * K + k] = first[k] ? __popcll(m_e[w * E2 + key[k]] & below) : -1;
-    if (a.ht)
-      for (int n = 0; n < N; ++n)
-        a.rank_n[i * N + n] = ((nodes >> n) & 1) ? __popcll(m_n[w * N + n] & below) : -1;
+    for (int k = 0; k < KMAX; ++k) re[k] = first[k] ? __popcll(m_e[w * E2 + key[k]] & below) : -1;
+    if constexpr (KMAX == 8) {
+      if (vec8) {
+        int4* dst = reinterpret_cast<int4*>(a.rank_e + i * 8);
+        dst[0] = int4{re[0], re[1], re[2], re[3]};
+        dst[1] = int4{re[4], re[5], re[6], re[7]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (k < K) a.rank_e[i * K + k] = re[k];
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < KMAX; ++k)
+        if (k < K) a.rank_e[i * K + k] = re[k];
+    }
+    if (a.ht) {
+      if (N == 8) {
+        int rn[8];
+#pragma unroll
+        for (int n = 0; n < 8; ++n) rn[n] = ((nodes >> n) & 1) ? __popcll(m_n[w * 8 + n] & below) : -1;
+        int4* dst = reinterpret_cast<int4*>(a.rank_n + i * 8);
+        dst[0] = int4{rn[0], rn[1], rn[2], rn[3]};
+        dst[1] = int4{rn[4], rn[5], rn[6], rn[7]};
+      } else {
+        for (int n = 0; n < N; ++n)
+          a.rank_n[i * N + n] = ((nodes >> n) & 1) ? __popcll(m_n[w * N + n] & below) : -1;
+      }
+    }
   }
 }
 

@@ -160,6 +160,14 @@ int dispatch_block_cap(const Group* g) {
   return g->cfg.num_cus > 0 ? g->cfg.num_cus * 4 : 0;
 }
 
+// log2(v) if v is a power of two, else -1.
+int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
 // The handle-dependent part of a dispatch launch.
 DispatchArgs dispatch_base(const Handle* h) {
   const Group* g = h->g;
@@ -490,6 +498,8 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.E2 = g->E2;
   a.L = g->L;
   a.s2_rank = g->s2_rank;
+  a.l_shift = log2_exact(g->L);
+  a.p_shift = log2_exact(g->P);
   a.tps = h->tps;
   a.n_tiles = h->n_tiles;
   a.hist_e = h->hist_e;
