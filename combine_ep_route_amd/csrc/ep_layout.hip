@@ -200,23 +200,28 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
   }
 }
 
-// One workgroup turns the tile histograms into exclusive prefix sums (the
-// kernel boundary makes the counts of every tile visible; no fences).
+// LL: the (expert, source) pairs are independent -- a source's slots for an
+// expert start at 0 -- so one thread per pair, over as many workgroups as it
+// takes: the prefix over the source's tiles, in place, and the pair's count.
+// Consecutive threads take consecutive experts (coalesced tile counts).
+__global__ __launch_bounds__(256) void layout_scan_ll_kernel(LayoutArgs a) {
+  const int E = a.E2, S = a.S, tps = a.tps;
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (x >= static_cast<int64_t>(E) * S) return;
+  const int e = static_cast<int>(x % E), src = static_cast<int>(x / E);
+  a.ll_count[static_cast<int64_t>(e) * S + src] =
+      chunk_prefix(a.hist_e, 0, tps, 0, [=](int tt) { return static_cast<int64_t>(src * tps + tt) * E + e; });
+}
+
+// HT: one workgroup turns the tile histograms into exclusive prefix sums
+// (the kernel boundary makes the counts of every tile visible; no fences).
 __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
   extern __shared__ int smem[];
   const int B = blockDim.x;
   const int tid = threadIdx.x;
   const int E = a.E2, N = a.N;   // stage-2 keys: the experts, or the ranks (per-rank HT)
   const int n_tiles = a.n_tiles;
-  if (!a.ht) {
-    // LL: per (expert, source), prefix over the source's own tiles.
-    for (int x = tid; x < E * a.S; x += B) {
-      const int e = x % E, src = x / E;
-      const int tps = a.tps;
-      a.ll_count[static_cast<int64_t>(e) * a.S + src] =
-          chunk_prefix(a.hist_e, 0, tps, 0, [=](int tt) { return static_cast<int64_t>(src * tps + tt) * E + e; });
-    }
-  } else {
+  {
     // HT.  Keys: the E stage-2 keys (sequence: every tile in order) and the R
     // stage-1 ranks d = n*G + g (sequence: the tiles of the sources at
     // position g, tps consecutive tiles per source).  A thread owns one
@@ -411,7 +416,12 @@ hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
   const size_t lds = count_lds_bytes(a.E2, a.N);
   if (a.K <= 8) layout_count_kernel<8><<<grid, block, lds, stream>>>(a);
   else layout_count_kernel<32><<<grid, block, lds, stream>>>(a);
-  layout_scan_kernel<<<dim3(1), dim3(kScanThreads), a.ht ? layout_scan_lds_bytes(a.E2, a.N, a.G, a.S, a.tps) : 0, stream>>>(a);
+  if (a.ht) {
+    layout_scan_kernel<<<dim3(1), dim3(kScanThreads), layout_scan_lds_bytes(a.E2, a.N, a.G, a.S, a.tps), stream>>>(a);
+  } else {
+    const int64_t pairs = static_cast<int64_t>(a.E2) * a.S;
+    layout_scan_ll_kernel<<<dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 
