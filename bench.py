@@ -117,14 +117,15 @@ def cpu_baseline(scores, x, weights, Y, n_tok):
                 seconds=round(dt, 3), tokens_per_s=round(n_tok / dt, 1))
 
 
-def ll_algorithmic_bytes(n_tok, K, H, E, S):
+def ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=True):
     """LL step bytes (every entry valid under the node limit):
     route    : scores n*E*4 read, topk n*K*4 written
     dispatch : tokens n*H*2 read, topk n*K*4 read, slot map n*K*4 written,
                counts E*S*4, messages n*K*(H + H/128*4 + 16) written
+               (BF16 payload: n*K*(2H + 16))
     combine  : n*K*H*2 read, weights + slot map 2*n*K*4 read, n*H*2 written
     """
-    msg = H + H // 128 * 4 + 16
+    msg = (H + H // 128 * 4 + 16) if fp8 else (2 * H + 16)
     route = n_tok * E * 4 + n_tok * K * 4
     dispatch = n_tok * H * 2 + 2 * n_tok * K * 4 + E * S * 4 + n_tok * K * msg
     combine = n_tok * K * H * 2 + 2 * n_tok * K * 4 + n_tok * H * 2
@@ -309,7 +310,7 @@ def run_ht(args, ep, per_rank=False):
     return result
 
 
-def run_ll(args, ep, S):
+def run_ll(args, ep, S, payload="fp8"):
     """The LL decode path, staged as in the NCCL-EP pipeline: route, handle,
     dispatch(send_only) + complete, combine(send_only) + complete."""
     w = I.LL_DECODE.with_(num_src_ranks=S)
@@ -336,7 +337,7 @@ def run_ll(args, ep, S):
 
     g = ep.ep_create_group(mode="ll", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
                            max_nodes_per_token=4, hidden=H, max_tokens_per_rank=T,
-                           num_src_ranks=S, payload="fp8", num_cus=args.num_cus)
+                           num_src_ranks=S, payload=payload, num_cus=args.num_cus)
     stream = torch.cuda.current_stream()
 
     def step(j, ev=None):
@@ -359,16 +360,19 @@ def run_ll(args, ep, S):
             ev[4].record(stream)
         ep.ep_destroy_handle(h)
 
-    ab = ll_algorithmic_bytes(n_tok, K, H, E, S)
+    ab = ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=payload == "fp8")
     mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
-    config = {"workload": f"ll_decode_{S}x{T}_plus_combine", "tokens": n_tok, "sources": S,
+    suffix = "" if payload == "fp8" else "_bf16"
+    config = {"workload": f"ll_decode_{S}x{T}{suffix}_plus_combine", "tokens": n_tok, "sources": S,
               "tokens_per_source": T, "hidden": H, "experts": E, "top_k": K, "nodes": 8,
               "ranks_per_node": 8, "max_nodes_per_token": 4, "slots": T,
               "algorithmic_bytes_per_step": ab["total"]}
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=False)
+    if payload != "fp8":
+        result["dtype"] = "bf16 payload / bf16 combine, fp32 accumulate"
     result["us_per_call"] = {k: round(float(v) * 1e3, 2)
                              for k, v in zip(["route", "handle", "dispatch", "combine"], mean_ms)}
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and payload == "fp8":
         log("[bench] timing the CPU oracle on one source's share")
         result["cpu_baseline"] = ll_cpu_baseline(T)
     ep.ep_destroy_group(g)
@@ -466,13 +470,14 @@ def main(argv=None):
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
                          "eager: every step is enqueued from Python")
     ap.add_argument("--workload", choices=["ht_prefill", "ht_prefill_rank", "ll_decode", "ll_decode_1src",
-                                           "ht_backward"],
+                                           "ll_decode_bf16", "ht_backward"],
                     default="ht_prefill",
                     help="ht_prefill: 4096 tokens, HT dispatch + combine (the headline); "
                          "ll_decode: 64 sources x 128 tokens, staged LL dispatch + combine; "
                          "ll_decode_1src: one source's 128 tokens; "
                          "ht_backward: the backward pass at the prefill shape on forward handles; "
-                         "ht_prefill_rank: the prefill step with the per-rank stage 2")
+                         "ht_prefill_rank: the prefill step with the per-rank stage 2; "
+                         "ll_decode_bf16: the 64 x 128 decode step with BF16 messages (14352 B)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters), then exit")
@@ -501,6 +506,8 @@ def main(argv=None):
         result = run_ht(args, ep, per_rank=args.workload == "ht_prefill_rank")
     elif args.workload == "ht_backward":
         result = run_ht_backward(args, ep)
+    elif args.workload == "ll_decode_bf16":
+        result = run_ll(args, ep, 64, payload="bf16")
     else:
         result = run_ll(args, ep, 64 if args.workload == "ll_decode" else 1)
     print(json.dumps(result), flush=True)

@@ -60,6 +60,11 @@ __device__ __forceinline__ Raw load_chunk(const DispatchArgs& p, int64_t i, int 
     r.a = active ? *reinterpret_cast<const u32x4*>(src + 16 * c) : zero;
     r.b = zero;
     r.scale = active ? p.x_scales[i * p.ld_s + (c >> 3)] : 0.0f;
+  } else if constexpr (IN == 1) {
+    // BF16 kept as BF16: a chunk is 8 values (16 bytes), a plain copy
+    const uint16_t* src = static_cast<const uint16_t*>(p.x) + i * p.ld_x;
+    r.a = active ? *reinterpret_cast<const u32x4*>(src + 8 * c) : zero;
+    r.b = zero;
   } else {
     const uint16_t* src = static_cast<const uint16_t*>(p.x) + i * p.ld_x;
     const u32x4* s4 = reinterpret_cast<const u32x4*>(src + 16 * c);
@@ -124,16 +129,12 @@ __device__ __forceinline__ void quantize(Raw& r) {
   r.a = out;
 }
 
-// Stores the 16 bytes of codes (or 32 bytes of bf16) of chunk c of a row.
+// Stores the 16 bytes of chunk c of a row (16 codes, or 8 bf16 values):
+// consecutive lanes write consecutive 16-byte pieces.
 template <int IN>
 __device__ __forceinline__ void put_codes(const Raw& r, uint8_t* row, int c, int C) {
   if (c >= C) return;
-  if constexpr (IN == 1) {
-    store_nt(r.a, row + 32 * c);
-    store_nt(r.b, row + 32 * c + 16);
-  } else {
-    store_nt(r.a, row + 16 * c);
-  }
+  store_nt(r.a, row + 16 * c);
 }
 
 // The wave's block scales, gathered so that one store instruction writes
@@ -188,13 +189,14 @@ __device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool p
   }
 }
 
-// One wave per token, four tokens per 256-thread workgroup; lane owns chunks
-// c = v*64 + lane, v < NV (16 elements each).  No barriers: everything
-// shared inside a token is a wave-uniform ballot result.
+// A token spans W waves, four waves per 256-thread workgroup; a lane owns
+// chunks c = v*64 + lane, v < NV, of its wave's range (16 elements each; 8
+// with a BF16 payload, a plain 16-byte copy).  No barriers: everything shared
+// inside a token is wave-uniform.
 template <int IN, bool HT, bool PAYLOAD, int KMAX, int NV>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
   const int lane = threadIdx.x & 63;
-  const int C = p.H / 16;
+  const int C = IN == 1 ? p.H / 8 : p.H / 16;   // 16-byte chunks of the payload row
   const int K = p.K, E = p.E, N = p.N;
   // Rows end on whole 128-byte lines when the scale bytes (H/32) are whole
   // 16-byte groups, so the LL header is 16-byte aligned: H % 512 == 0.
@@ -381,7 +383,7 @@ constexpr int kChunksPerLane = 4;
 
 template <int IN, bool PAYLOAD, int KMAX, int NV>
 void launch_nv(const DispatchArgs& p, hipStream_t stream) {
-  const int C = p.H / 16;
+  const int C = IN == 1 ? p.H / 8 : p.H / 16;
   const int W = PAYLOAD ? (C + 64 * NV - 1) / (64 * NV) : 1;
   int64_t blocks = (p.n * W + 3) / 4;
   if (p.max_blocks > 0 && blocks > p.max_blocks) blocks = p.max_blocks;
