@@ -370,6 +370,21 @@ def test_ht_dispatch_tiny(payload):
     ep.ep_destroy_group(g)
 
 
+def test_bf16_dispatch_full_hidden():
+    """BF16 payload at hidden 7168: a token spans four waves of 8-value
+    chunks, the last one ragged; HT rows and LL messages (header, zero tail)
+    equal the oracle's."""
+    w = I.HT_PREFILL.with_(tokens_per_rank=300, payload="bf16", seed=43)
+    say("HT dispatch BF16 hidden 7168 (sampled rows)")
+    rng = np.random.default_rng(44)
+    sample = np.sort(rng.choice(300, size=48, replace=False))
+    g, _, _ = _ht_dispatch(w, I.tokens_for(w), I.scores_for(w), I.normal_weights(300, 8, 43), sample=sample)
+    ep.ep_destroy_group(g)
+    say("LL dispatch BF16 hidden 7168 (sampled tokens)")
+    _ll_dispatch(2, 64, 256, 8, 7168, "bf16", 64, seed=45, N=8, G=8, M=4,
+                 sample=np.sort(rng.choice(128, size=24, replace=False)))
+
+
 def test_ht_dispatch_prequantised_input():
     w = I.HT_PREFILL.with_(tokens_per_rank=300, hidden=512, seed=41)
     say("HT dispatch with FP8 input + scales")
