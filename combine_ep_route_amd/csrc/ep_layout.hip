@@ -359,16 +359,22 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
 }
 
 // Receive stage of a dispatch: the per-(expert, source) counters [E, S] as
-// they are, or summed over the sources (tokens per expert).
+// they are (one thread per counter), or summed over the sources (tokens per
+// expert): one wave per expert, lanes over the sources (coalesced), then a
+// shuffle reduction.
 __global__ void recv_counts_kernel(const int32_t* counts, int E, int S, int per_expert, int32_t* out) {
-  const int x = blockIdx.x * blockDim.x + threadIdx.x;
   if (per_expert) {
-    if (x >= E) return;
+    const int e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (e >= E) return;
     int sum = 0;
-    for (int s = 0; s < S; ++s) sum += counts[static_cast<int64_t>(x) * S + s];
-    out[x] = sum;
-  } else if (x < E * S) {
-    out[x] = counts[x];
+    for (int s = lane; s < S; s += 64) sum += counts[static_cast<int64_t>(e) * S + s];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) sum += __shfl_xor(sum, off, 64);
+    if (lane == 0) out[e] = sum;
+  } else {
+    const int64_t x = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (x < static_cast<int64_t>(E) * S) out[x] = counts[x];
   }
 }
 
@@ -396,9 +402,10 @@ size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps) {
 
 hipError_t launch_recv_counts(const int32_t* counts, int E, int S, int per_expert, int32_t* out,
                               hipStream_t stream) {
-  const int items = per_expert ? E : E * S;
+  const int64_t items = per_expert ? static_cast<int64_t>(E) * 64 : static_cast<int64_t>(E) * S;   // threads
   if (items <= 0) return hipSuccess;
-  recv_counts_kernel<<<dim3((items + 255) / 256), dim3(256), 0, stream>>>(counts, E, S, per_expert, out);
+  recv_counts_kernel<<<dim3(static_cast<unsigned>((items + 255) / 256)), dim3(256), 0, stream>>>(counts, E, S,
+                                                                                              per_expert, out);
   return hipGetLastError();
 }
 
