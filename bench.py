@@ -178,6 +178,7 @@ def time_steps(step, args, stream, out_of, ep, g, n_calls=4):
     per = np.array([[events[j][q].elapsed_time(events[j][q + 1]) for q in range(n_calls)]
                     for j in range(args.steps)])  # ms
     mean_ms = per.mean(axis=0)
+    pct = {q: np.percentile(per, q, axis=0) for q in (10, 50, 90)}
     ms_per_step = ms_eager
     if args.mode == "graph":
         graph = torch.cuda.CUDAGraph()
@@ -205,10 +206,38 @@ def time_steps(step, args, stream, out_of, ep, g, n_calls=4):
         step(0)
         torch.cuda.synchronize()
         assert torch.equal(ref.view(torch.int16), out_of(0).view(torch.int16))
-    return mean_ms, ms_eager, ms_per_step
+    return mean_ms, ms_eager, ms_per_step, pct
 
 
-def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok):
+def percentiles_ms(names, pct):
+    """Per-call p10 / median / p90 of the eager event timings, in ms."""
+    return {k: {f"p{q}": round(float(pct[q][i]), 5) for q in (10, 50, 90)} for i, k in enumerate(names)}
+
+
+def time_cpu_sync(ep, g, s, reps=50):
+    """The HT receive-count query, the pages' CPU synchronisation, timed on
+    the host apart from the step: `wait` is the blocking call alone on a
+    finished handle (stream sync + device-to-host copy of the counts);
+    `route_handle_wait` runs from enqueueing route + handle until the count
+    is on the host."""
+    wait, full = [], []
+    for _ in range(reps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ep.ep_route(g, s["scores"], s["topk"])
+        h = ep.ep_create_handle(g, s["topk"])
+        ep.ep_handle_get_num_recv(h, -1)
+        t1 = time.perf_counter()
+        ep.ep_handle_get_num_recv(h, -1)
+        t2 = time.perf_counter()
+        ep.ep_destroy_handle(h)
+        full.append(t1 - t0)
+        wait.append(t2 - t1)
+    q = lambda a: {f"p{p}": round(float(np.percentile(a, p)) * 1e6, 2) for p in (10, 50, 90)}
+    return {"wait": q(wait), "route_handle_wait": q(full)}
+
+
+def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok, pct):
     names = ["route", "handle", "dispatch", "combine"]
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
     dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
@@ -233,6 +262,7 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
         "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": {k: round(float(v), 5) for k, v in zip(names, mean_ms)},
+        "kernel_ms_percentiles": percentiles_ms(names, pct),
         "kernel_gbs": {"route": round(ab["route"] / (mean_ms[0] * 1e-3) / 1e9, 1),
                        "dispatch": round(ab["dispatch"] / (mean_ms[2] * 1e-3) / 1e9, 1),
                        "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
@@ -295,12 +325,14 @@ def run_ht(args, ep, per_rank=False):
     ep.ep_destroy_handle(h)
     ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank)
 
-    mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
+    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
     config = {"workload": "ht_prefill_4096_per_rank_plus_combine" if per_rank else "ht_prefill_4096_plus_combine",
               "tokens": n_tok, "hidden": H, "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
               "max_nodes_per_token": 4, "stage2": "per_rank" if per_rank else "per_expert",
               "stage1_rows": rows1, "stage2_rows": rows2, "algorithmic_bytes_per_step": ab["total"]}
-    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=not per_rank)
+    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=not per_rank,
+                         pct=pct)
+    result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
         result["dtype"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
     if not args.no_cpu_baseline and not per_rank:
@@ -361,13 +393,13 @@ def run_ll(args, ep, S, payload="fp8"):
         ep.ep_destroy_handle(h)
 
     ab = ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=payload == "fp8")
-    mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
+    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
     suffix = "" if payload == "fp8" else "_bf16"
     config = {"workload": f"ll_decode_{S}x{T}{suffix}_plus_combine", "tokens": n_tok, "sources": S,
               "tokens_per_source": T, "hidden": H, "experts": E, "top_k": K, "nodes": 8,
               "ranks_per_node": 8, "max_nodes_per_token": 4, "slots": T,
               "algorithmic_bytes_per_step": ab["total"]}
-    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=False)
+    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=False, pct=pct)
     if payload != "fp8":
         result["dtype"] = "bf16 payload / bf16 combine, fp32 accumulate"
     result["us_per_call"] = {k: round(float(v) * 1e3, 2)
@@ -426,8 +458,8 @@ def run_ht_backward(args, ep):
 
     cb = n_tok * H * 2 + 2 * rows2 * H * 2 + 3 * n_tok * K * 4
     db = rows2 * H * 2 + n_tok * K * 4 + n_tok * H * 2
-    mean_ms, ms_eager, ms_per_step = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g,
-                                                n_calls=2)
+    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g,
+                                                     n_calls=2)
     total = cb + db
     value = total / (ms_per_step * 1e-3) / 1e9
     dom, dom_b, dom_ms = ("combine_backward", cb, mean_ms[0]) if mean_ms[0] >= mean_ms[1] else \
@@ -447,6 +479,7 @@ def run_ht_backward(args, ep):
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": {"combine_backward": round(float(mean_ms[0]), 5),
                       "dispatch_backward": round(float(mean_ms[1]), 5)},
+        "kernel_ms_percentiles": percentiles_ms(["combine_backward", "dispatch_backward"], pct),
         "kernel_gbs": {"combine_backward": round(cb / (mean_ms[0] * 1e-3) / 1e9, 1),
                        "dispatch_backward": round(db / (mean_ms[1] * 1e-3) / 1e9, 1)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
