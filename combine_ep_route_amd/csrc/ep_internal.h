@@ -148,6 +148,7 @@ struct LayoutArgs {
   int s2_rank;           // HT stage 2 per (token, rank): key = e / L, first entry only
   int l_shift, p_shift;  // log2 of L and P when powers of two, else -1
   int tps, n_tiles;
+  int ll_fused;          // LL, one workgroup per source: the count kernel also writes the prefixes and counts
   int32_t* hist_e;
   int32_t* hist_n;
   int32_t* topk_copy;    // [n, K]

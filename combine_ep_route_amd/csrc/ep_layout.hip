@@ -18,6 +18,9 @@
 //     per tile), stored in the handle; the dispatch kernel adds rank and
 //     tile prefix.
 // Neither half uses atomics on positions, so every map is bit-reproducible.
+// LL slots restart at 0 for every (expert, source), so no prefix crosses a
+// source: when a source has at most kCountWaves tiles, one count workgroup
+// holds all of them and writes the prefixes and counts too (one launch).
 #include "ep_internal.h"
 
 namespace ep {
@@ -159,7 +162,18 @@ __global__ __launch_bounds__(256) void layout_count_kernel(LayoutArgs a) {
         if ((nodes >> n) & 1) atomicOr(reinterpret_cast<unsigned long long*>(&m_n[w * N + n]), bit);
   }
   __syncthreads();
-  if (tile_ok) {
+  if (a.ll_fused) {
+    // Workgroup = source blockIdx.x, wave q = its tile q: the exclusive
+    // prefix over the earlier tiles and the (expert, source) count.
+    for (int e = tid; e < E2; e += blockDim.x) {
+      int run = 0;
+      for (int q = 0; q < nw; ++q) {
+        a.hist_e[(static_cast<int64_t>(blockIdx.x) * nw + q) * E2 + e] = run;
+        run += __popcll(m_e[q * E2 + e]);
+      }
+      a.ll_count[static_cast<int64_t>(e) * a.S + blockIdx.x] = run;
+    }
+  } else if (tile_ok) {
     for (int e = lane; e < E2; e += 64) a.hist_e[static_cast<int64_t>(j) * E2 + e] = __popcll(m_e[w * E2 + e]);
     if (a.ht)
       for (int n = lane; n < N; n += 64) a.hist_n[static_cast<int64_t>(j) * N + n] = __popcll(m_n[w * N + n]);
@@ -387,8 +401,6 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t value) {
 constexpr int kCountWaves = 4;     // tiles per count workgroup
 constexpr int kScanThreads = 1024;
 
-size_t count_lds_bytes(int E, int N) { return static_cast<size_t>(kCountWaves) * (E + N) * 8; }
-
 }  // namespace
 
 size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps) {
@@ -417,12 +429,18 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream) {
-  if (a.n == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>((a.n_tiles + kCountWaves - 1) / kCountWaves)), block(kCountWaves * 64);
-  const size_t lds = count_lds_bytes(a.E2, a.N);
+hipError_t launch_layout(const LayoutArgs& a_in, hipStream_t stream) {
+  if (a_in.n == 0) return hipSuccess;
+  LayoutArgs a = a_in;
+  a.ll_fused = !a.ht && a.tps <= kCountWaves;
+  // Fused LL: one workgroup per source, one wave per tile of the source.
+  const int waves = a.ll_fused ? a.tps : kCountWaves;
+  const dim3 grid(static_cast<unsigned>(a.ll_fused ? a.S : (a.n_tiles + kCountWaves - 1) / kCountWaves));
+  const dim3 block(waves * 64);
+  const size_t lds = static_cast<size_t>(waves) * (a.E2 + a.N) * 8;
   if (a.K <= 8) layout_count_kernel<8><<<grid, block, lds, stream>>>(a);
   else layout_count_kernel<32><<<grid, block, lds, stream>>>(a);
+  if (a.ll_fused) return hipGetLastError();
   if (a.ht) {
     layout_scan_kernel<<<dim3(1), dim3(kScanThreads), layout_scan_lds_bytes(a.E2, a.N, a.G, a.S, a.tps), stream>>>(a);
   } else {
