@@ -19,7 +19,7 @@
 //     tile prefix.
 // Neither half uses atomics on positions, so every map is bit-reproducible.
 // LL slots restart at 0 for every (expert, source), so no prefix crosses a
-// source: when a source has at most kCountWaves tiles, one count workgroup
+// source: when a source has at most kLlFusedTiles tiles, one count workgroup
 // holds all of them and writes the prefixes and counts too (one launch).
 #include "ep_internal.h"
 
@@ -398,7 +398,8 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t count, int32_t value) {
     p[x] = value;
 }
 
-constexpr int kCountWaves = 4;     // tiles per count workgroup
+constexpr int kCountWaves = 1;     // tiles per count workgroup (one wave: the tiles spread over CUs)
+constexpr int kLlFusedTiles = 4;   // LL: a source of at most this many tiles is one workgroup
 constexpr int kScanThreads = 1024;
 
 }  // namespace
@@ -432,7 +433,7 @@ hipError_t launch_fill_i32(int32_t* p, int64_t count, int32_t value, hipStream_t
 hipError_t launch_layout(const LayoutArgs& a_in, hipStream_t stream) {
   if (a_in.n == 0) return hipSuccess;
   LayoutArgs a = a_in;
-  a.ll_fused = !a.ht && a.tps <= kCountWaves;
+  a.ll_fused = !a.ht && a.tps <= kLlFusedTiles;
   // Fused LL: one workgroup per source, one wave per tile of the source.
   const int waves = a.ll_fused ? a.tps : kCountWaves;
   const dim3 grid(static_cast<unsigned>(a.ll_fused ? a.S : (a.n_tiles + kCountWaves - 1) / kCountWaves));
