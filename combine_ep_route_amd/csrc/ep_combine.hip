@@ -85,11 +85,13 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineArgs a) {
 //   dY[loc(t,k)] chunk = bf16_rne(w[t,k] * g chunk)   (one fp32 multiply)
 //   dw[t,k] = sum over the row of g * Y[loc(t,k)]     (per-thread fp32 fma
 //             chains, then a fixed-order shuffle/LDS tree: deterministic)
-// The gradient chunk is loaded once and serves all K entries; expert rows
-// and row gradients stream past the caches (non-temporal).
+// The gradient chunk is loaded once and serves all K entries; the chunk's K
+// expert-row loads are all issued before its first row-gradient store (the
+// compiler may not move a load above a store it cannot prove disjoint).
+// Expert rows and row gradients stream past the caches (non-temporal).
 template <int KMAX>
-__global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a) {
-  __shared__ float red[KMAX][4];
+__global__ __launch_bounds__(KMAX <= 8 ? 1024 : 256) void combine_backward_kernel(CombineBwdArgs a) {
+  __shared__ float red[KMAX][16];
   const int C = a.H / 8;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwave = blockDim.x >> 6;
   for (int64_t i = blockIdx.x; i < a.n; i += gridDim.x) {
@@ -112,6 +114,15 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a)
         gf[2 * q] = __uint_as_float(gv[q] << 16);
         gf[2 * q + 1] = __uint_as_float(gv[q] & 0xFFFF0000u);
       }
+      // every expert-row load is issued before the first row-gradient store
+      u32x4 yv[KMAX];
+      if (a.y) {
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          yv[k] = ok[k] ? __builtin_nontemporal_load(
+                              reinterpret_cast<const u32x4*>(a.y + static_cast<int64_t>(r[k]) * a.ld_y + 8 * c))
+                        : u32x4{0, 0, 0, 0};
+      }
 #pragma unroll
       for (int k = 0; k < KMAX; ++k) {
         if (!ok[k]) continue;
@@ -120,12 +131,10 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(CombineBwdArgs a)
         for (int q = 0; q < 4; ++q) o[q] = pack_bf16x2(wk[k] * gf[2 * q], wk[k] * gf[2 * q + 1]);
         __builtin_nontemporal_store(o, reinterpret_cast<u32x4*>(a.dy + static_cast<int64_t>(r[k]) * a.ld_dy + 8 * c));
         if (a.y) {
-          const u32x4 yv = __builtin_nontemporal_load(
-              reinterpret_cast<const u32x4*>(a.y + static_cast<int64_t>(r[k]) * a.ld_y + 8 * c));
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            dot[k] = __builtin_fmaf(gf[2 * q], __uint_as_float(yv[q] << 16), dot[k]);
-            dot[k] = __builtin_fmaf(gf[2 * q + 1], __uint_as_float(yv[q] & 0xFFFF0000u), dot[k]);
+            dot[k] = __builtin_fmaf(gf[2 * q], __uint_as_float(yv[k][q] << 16), dot[k]);
+            dot[k] = __builtin_fmaf(gf[2 * q + 1], __uint_as_float(yv[k][q] & 0xFFFF0000u), dot[k]);
           }
         }
       }
@@ -216,10 +225,18 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
 hipError_t launch_combine_backward(const CombineBwdArgs& a, hipStream_t stream) {
   if (a.n == 0) return hipSuccess;
   const int C = a.H / 8;
-  // at most 4 waves; whole chunks per thread where H allows
+  // Whole chunks per thread where H allows.  With K <= 8, up to 7 waves per
+  // token (hidden 7168: two chunks per thread, 189 us against 207 us with 2
+  // waves x 7 chunks at 4096 tokens); with more entries the K preloaded rows
+  // take the registers, so at most 4 waves.
   int threads = 256;
-  for (int cand : {256, 192, 128})
-    if (C % cand == 0) { threads = cand; break; }
+  if (a.K <= 8) {
+    for (int cand : {448, 384, 320, 256, 192, 128})
+      if (C % cand == 0) { threads = cand; break; }
+  } else {
+    for (int cand : {256, 192, 128})
+      if (C % cand == 0) { threads = cand; break; }
+  }
   if (C < threads) threads = ((C + 63) / 64) * 64;
   int64_t blocks = a.n;
   if (a.max_blocks > 0 && blocks > a.max_blocks) blocks = a.max_blocks;
