@@ -217,8 +217,8 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t stream) {
   }
   if (rows > 65535) rows = 65535;
   const dim3 grid(col_blocks, static_cast<unsigned>(rows)), block(threads);
-  if (a.K <= 8) combine_kernel<8><<<grid, block, 0, stream>>>(a);
-  else combine_kernel<8><<<grid, block, 0, stream>>>(a);
+  // Batches of 8 entries: K <= 8 is one batch, larger K loops over batches.
+  combine_kernel<8><<<grid, block, 0, stream>>>(a);
   return hipGetLastError();
 }
 
