@@ -17,6 +17,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <vector>
 
 #include "ep_internal.h"
 
@@ -716,6 +717,40 @@ EP_API ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_te
   const bool ll = h->g->cfg.mode == EP_MODE_LL;
   if (ll && which == EP_BUF_LL_RECV && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;
   return buffer_view(h->g, which, ll ? h->ll_half : 0, view);
+}
+
+EP_API ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t which, ep_tensor_t* view) {
+  Handle* h = reinterpret_cast<Handle*>(handle);
+  if (!handle_ok(h) || !view) return EP_ERR_INVALID_ARGUMENT;
+  Group* g = h->g;
+  if (rank < 0 || rank >= g->R) return EP_ERR_INVALID_ARGUMENT;
+  const bool ll = g->cfg.mode == EP_MODE_LL;
+  if (ll && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;   // not dispatched: no buffer yet
+  ep_tensor_t full;
+  if (const ep_status_t st = buffer_view(g, which, ll ? h->ll_half : 0, &full); st != EP_OK) return st;
+  int64_t first = 0, count = 0;
+  if (ll) {
+    // Rank r's experts [r*L, (r+1)*L) are one contiguous [L][S][T_max] block of slots.
+    count = static_cast<int64_t>(g->L) * g->cfg.num_src_ranks * g->cfg.max_tokens_per_rank;
+    first = rank * count;
+  } else {
+    // The rank's rows [offset, offset + count) from the handle's counts.
+    const bool stage1 = which >= EP_BUF_HT_STAGE1 && which <= EP_BUF_HT_STAGE1_WEIGHTS;
+    const int keys = stage1 || g->s2_rank ? 1 : g->L;   // stage 2 per expert: the rank's L experts
+    const int k0 = stage1 || g->s2_rank ? rank : rank * g->L;
+    std::vector<int32_t> c(static_cast<size_t>(keys));
+    int32_t off = 0;
+    EP_HIP(hipStreamSynchronize(h->stream));
+    EP_HIP(hipMemcpy(&off, (stage1 ? h->off1 : h->off2) + k0, sizeof(int32_t), hipMemcpyDeviceToHost));
+    EP_HIP(hipMemcpy(c.data(), (stage1 ? h->c1 : h->c2) + k0, keys * sizeof(int32_t), hipMemcpyDeviceToHost));
+    first = off;
+    for (int32_t v : c) count += v;
+  }
+  // Row `first` of the view starts strides[0] elements per row further in.
+  full.data = static_cast<uint8_t*>(full.data) + first * full.strides[0] * dtype_size(full.dtype);
+  full.sizes[0] = count;
+  *view = full;
+  return EP_OK;
 }
 
 // ===========================================================================

@@ -267,3 +267,9 @@ def ep_handle_get_buffer(handle: Handle, which: int) -> torch.Tensor:
     d = A.EpTensor()
     _check("ep_handle_get_buffer", A.lib().ep_handle_get_buffer(handle.ptr, which, ctypes.byref(d)))
     return _as_torch(d)
+
+
+def ep_get_partition(handle: Handle, rank: int, which: int) -> torch.Tensor:
+    d = A.EpTensor()
+    _check("ep_get_partition", A.lib().ep_get_partition(handle.ptr, rank, which, ctypes.byref(d)))
+    return _as_torch(d)

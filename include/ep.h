@@ -312,6 +312,26 @@ ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
  * buffers).  EP_ERR_INVALID_ARGUMENT for an LL handle not yet dispatched. */
 ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t *view);
 
+/* One destination rank's partition of a receive buffer: the view of
+ * ep_handle_get_buffer narrowed to the rows or slots rank `rank` receives
+ * ("NVSHMEM and DeepEP", low-latency and high-throughput sections: each rank
+ * owns the receive region of its local experts; the 64 ranks are partitions
+ * of this GPU's memory).
+ *   LL (EP_BUF_LL_RECV): the rank's [E/R][S][T_max] block of message slots,
+ *       [E/R*S*T_max, row+16], of the buffer the handle's dispatch wrote;
+ *       which slots hold messages is given by EP_MAP_LL_COUNT.
+ *   HT, stage 1 (EP_BUF_HT_STAGE1*): the rank's stage-1 rows, offset and
+ *       count from EP_MAP_HT_RANK_OFFSET / _COUNT.
+ *   HT, stage 2 (EP_BUF_HT_STAGE2*): the rows of the rank's E/R experts (with
+ *       the per-rank stage 2: the rank's rows), expert after expert.
+ * The view is taken from the handle (HT bounds are this routing's counts),
+ * so the HT forms synchronise the handle's stream and read two counters, as
+ * ep_handle_get_num_recv does; the LL form does not block.  The rows hold
+ * data once the handle's dispatch has run.  EP_ERR_INVALID_ARGUMENT for a
+ * rank outside [0, R), a buffer id of the other mode, or an LL handle not
+ * yet dispatched. */
+ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t which, ep_tensor_t *view);
+
 /* ----------------------------------------------------------------------- */
 /* Combine (A7)                                                              */
 /* ----------------------------------------------------------------------- */

@@ -199,6 +199,7 @@ def test_staged_calls_reject_null_handles():
     view = A.EpTensor()
     assert lib.ep_complete(None, None) == A.EP_ERR_INVALID_ARGUMENT
     assert lib.ep_handle_get_buffer(None, A.EP_BUF_LL_RECV, ctypes.byref(view)) == A.EP_ERR_INVALID_ARGUMENT
+    assert lib.ep_get_partition(None, 0, A.EP_BUF_LL_RECV, ctypes.byref(view)) == A.EP_ERR_INVALID_ARGUMENT
 
 
 def _t(data, dtype, sizes, strides=None, tag=A.EP_TAG_NONE):

@@ -1,0 +1,159 @@
+"""One destination rank's partition of the receive buffers, GPU vs oracle.
+
+"NVSHMEM and DeepEP: GPU-initiated communication", low-latency and
+high-throughput sections: every rank owns the receive region of its local
+experts (LL: a [local expert][source][slot] block; HT: the rows that reach
+it).  With the 64 ranks as partitions of one GPU's memory, ep_get_partition
+narrows the group's buffers to one rank: each view must be exactly that
+rank's slice of the full buffer, hold the oracle's rows for the entries
+routed to that rank, and the partitions together must tile the buffer.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import A, I, buffer, dev, ep, host, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+def _ht_group(S, T, E, N, G, K, H, stage2="expert"):
+    return ep.ep_create_group(mode="ht", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                              max_nodes_per_token=0, hidden=H, max_tokens_per_rank=T, num_src_ranks=S,
+                              payload="fp8", ht_stage2=stage2)
+
+
+def test_ht_partitions_are_the_ranks_rows():
+    S, T, E, N, G, K, H = 3, 200, 64, 4, 2, 4, 256
+    R, L = N * G, E // (N * G)
+    say(f"HT partitions: S={S} T={T} E={E} R={R} K={K} H={H}")
+    x = I.normal_bf16(S * T, H, 71)
+    topk = I.random_topk(S * T, E, K, seed=72)
+    g = _ht_group(S, T, E, N, G, K, H)
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        ep.ep_dispatch(h, x.cuda())
+        lay = oracle.layout_ht(topk, S, E, N, G)
+        img = oracle.token_rows(I.bf16_bits(x), True)
+        st1, st2 = buffer(g, A.EP_BUF_HT_STAGE1), buffer(g, A.EP_BUF_HT_STAGE2)
+        tok1_all = host(buffer(g, A.EP_BUF_HT_STAGE1_TOKEN))
+        src2_all = host(buffer(g, A.EP_BUF_HT_STAGE2_SRC))
+        n1 = n2 = 0
+        for r in range(R):
+            # stage 1: the rows of destination rank r
+            o, c = int(lay["off1"][r]), int(lay["c1"][r])
+            p1 = ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE1)
+            assert tuple(p1.shape) == (c, st1.shape[1])
+            if c:
+                assert p1.data_ptr() == st1[o].data_ptr()
+            rows = host(p1)
+            for i, n in zip(*np.nonzero((lay["node_row"] >= o) & (lay["node_row"] < o + c))):
+                np.testing.assert_array_equal(rows[lay["node_row"][i, n] - o], img[i], err_msg=f"rank {r} token {i}")
+            np.testing.assert_array_equal(host(ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE1_TOKEN)),
+                                          tok1_all[o:o + c])
+            assert tuple(ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE1_TOPK).shape) == (c, K)
+            # stage 2: the rows of rank r's L experts, expert after expert
+            o2, c2 = int(lay["off2"][r * L]), int(lay["c2"][r * L:(r + 1) * L].sum())
+            p2 = ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE2)
+            assert tuple(p2.shape) == (c2, st2.shape[1])
+            if c2:
+                assert p2.data_ptr() == st2[o2].data_ptr()
+            rows2 = host(p2)
+            inside = (lay["row2"] >= o2) & (lay["row2"] < o2 + c2)
+            assert int(inside.sum()) == c2
+            for i, k in zip(*np.nonzero(inside)):
+                assert topk[i, k] // L == r
+                np.testing.assert_array_equal(rows2[lay["row2"][i, k] - o2], img[i], err_msg=f"rank {r} entry {i},{k}")
+            np.testing.assert_array_equal(host(ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE2_SRC)),
+                                          src2_all[o2:o2 + c2])
+            n1 += c
+            n2 += c2
+        assert n1 == int(lay["c1"].sum()) and n2 == S * T * K
+        for bad_rank in (-1, R):
+            with pytest.raises(ep.EpError) as ei:
+                ep.ep_get_partition(h, bad_rank, A.EP_BUF_HT_STAGE1)
+            assert ei.value.status == A.EP_ERR_INVALID_ARGUMENT
+        with pytest.raises(ep.EpError):
+            ep.ep_get_partition(h, 0, A.EP_BUF_LL_RECV)          # an LL buffer id in HT
+        with pytest.raises(ep.EpError):
+            ep.ep_get_partition(h, 0, A.EP_BUF_HT_STAGE2_TOPK)   # exists only with the per-rank stage 2
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_ht_per_rank_stage2_partitions():
+    S, T, E, N, G, K, H = 2, 150, 64, 4, 2, 6, 128
+    R, L = N * G, E // (N * G)
+    say(f"HT per-rank stage-2 partitions: S={S} T={T} E={E} R={R} K={K}")
+    x = I.normal_bf16(S * T, H, 73)
+    topk = I.random_topk(S * T, E, K, seed=74)
+    g = _ht_group(S, T, E, N, G, K, H, stage2="rank")
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        ep.ep_dispatch(h, x.cuda())
+        lay = oracle.layout_ht_rank(topk, S, E, R)
+        total = 0
+        for r in range(R):
+            o, c = int(lay["off2"][r]), int(lay["c2"][r])
+            p = ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE2_TOPK)
+            assert tuple(p.shape) == (c, K)
+            ids = host(p)
+            assert ((ids >= -1) & (ids < L)).all()
+            # every row carries at least one entry of the rank (its first one)
+            assert (ids >= 0).any(axis=1).all()
+            assert tuple(ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE2).shape)[0] == c
+            total += c
+        assert total == int(lay["c2"].sum())
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_ll_partitions_follow_the_handles_buffer():
+    S, T, E, N, G, K, H, slots = 2, 50, 32, 2, 2, 4, 256, 64
+    R, L = N * G, E // (N * G)
+    per = L * S * slots
+    say(f"LL partitions: S={S} T={T} E={E} R={R} K={K} slots={slots}")
+    x = I.normal_bf16(S * T, H, 75)
+    topk = I.random_topk(S * T, E, K, seed=76)
+    g = ep.ep_create_group(mode="ll", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=0, hidden=H, max_tokens_per_rank=slots, num_src_ranks=S,
+                           payload="fp8", max_handles=3)
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        with pytest.raises(ep.EpError):
+            ep.ep_get_partition(h, 0, A.EP_BUF_LL_RECV)          # not dispatched yet
+        ep.ep_dispatch(h, x.cuda())
+        _, slot, _ = oracle.layout_ll(topk, S, E, slots)
+        img = oracle.token_rows(I.bf16_bits(x), True)
+        rb = img.shape[1]
+        full = ep.ep_handle_get_buffer(h, A.EP_BUF_LL_RECV)
+        for r in range(R):
+            p = ep.ep_get_partition(h, r, A.EP_BUF_LL_RECV)
+            assert tuple(p.shape) == (per, full.shape[1])
+            assert p.data_ptr() == full[r * per].data_ptr()
+            msgs = host(p)
+            for i, k in zip(*np.nonzero(topk // L == r)):
+                m = slot[i, k] - r * per
+                assert 0 <= m < per
+                np.testing.assert_array_equal(msgs[m, :rb], img[i], err_msg=f"rank {r} entry {i},{k}")
+                assert list(msgs[m, rb:rb + 16].view(np.int32)) == [i % T, i // T, k, 0]
+        with pytest.raises(ep.EpError):
+            ep.ep_get_partition(h, 0, A.EP_BUF_HT_STAGE1)        # an HT buffer id in LL
+        # the next dispatch takes the other receive buffer; each handle's view follows its own
+        h2 = ep.ep_create_handle(g, dev(topk))
+        ep.ep_dispatch(h2, x.cuda())
+        assert ep.ep_get_partition(h2, 1, A.EP_BUF_LL_RECV).data_ptr() != \
+            ep.ep_get_partition(h, 1, A.EP_BUF_LL_RECV).data_ptr()
+        torch.cuda.synchronize()
+        ep.ep_destroy_handle(h2)
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
