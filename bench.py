@@ -263,6 +263,12 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "kernel_ms": {k: round(float(v), 5) for k, v in zip(names, mean_ms)},
         "kernel_ms_percentiles": percentiles_ms(names, pct),
+        # dispatch + combine alone at their median per-call times (route and
+        # handle excluded): tokens / (t_dispatch + t_combine) and the bytes of
+        # the two over the same time
+        "dispatch_combine_median": {
+            "tokens_per_s": round(n_tok / ((pct[50][2] + pct[50][3]) * 1e-3), 1),
+            "gbs": round((ab["dispatch"] + ab["combine"]) / ((pct[50][2] + pct[50][3]) * 1e-3) / 1e9, 1)},
         "kernel_gbs": {"route": round(ab["route"] / (mean_ms[0] * 1e-3) / 1e9, 1),
                        "dispatch": round(ab["dispatch"] / (mean_ms[2] * 1e-3) / 1e9, 1),
                        "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
