@@ -74,10 +74,16 @@ def algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank=False):
 
 
 def source_digest():
+    """Digest of the dispatch and combine sources' code: line comments,
+    trailing blanks and empty lines are left out, so that only a change of
+    code makes the stored counter readings stale."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "combine_ep_route_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "combine_ep_route_amd", "csrc", name)) as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -11,22 +11,27 @@
 // sizes 7408 B (FP8) / 14352 B (BF16).
 //
 // Mapping: a token is split over W waves, each owning a contiguous range of
-// 64*NV 16-element chunks (lane l: chunks c0 + v*64, v < NV); four waves per
-// 256-thread workgroup and no barriers -- each wave ranks its token itself.
+// 64*NV chunks (16 elements; 8 with a BF16 payload; lane l: chunks
+// c0 + v*64, v < NV); four waves per 256-thread workgroup and no barriers --
+// each wave ranks its token itself.
 //  1. The token's payload loads are issued first (16-byte loads).
-//  2. Its rank inside its 64-token tile (from the handle) plus the tile's
-//     prefix gives every slot / row.  Positions are wave-uniform.
-//  3. A 128-element block is 8 consecutive lanes; its amax is a 3-step
+//  2. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 (IEEE fp32 division)
 //     and q = E4M3(x/scale), the quotient by a refined reciprocal and one
 //     fused residual correction (equal to the IEEE quotient's codes on the
-//     whole bf16 domain, which the tests sweep).
+//     whole bf16 domain, which the tests sweep).  Quantising comes before
+//     the positions, so the raw chunks' registers are free early.
+//  3. The token's rank inside its 64-token tile (from the handle) plus the
+//     tile's prefix gives every slot / row.  Positions are wave-uniform.
 //  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
-//     size rounded up to 128 B; the padding is never written).  Each chunk
-//     of codes goes to every destination row with non-temporal stores
-//     (nothing on this GPU reads the rows back during the pass); the
-//     wave's block scales are gathered into its first lanes and written by
-//     one store instruction (16 bytes per 4 blocks).
+//     size rounded up to 128 B).  Each chunk of codes goes to every
+//     destination row with non-temporal stores (nothing on this GPU reads
+//     the rows back during the pass).  When H is a multiple of 512 the
+//     token's last wave writes each row's last 128-byte line whole: scales,
+//     LL header, zeros up to the pitch, so that no line is written in part.
+//     Otherwise the wave's block scales are gathered into its first lanes
+//     and written by one store instruction (16 bytes per 4 blocks), and the
+//     padding is never written.
 #include "ep_internal.h"
 
 namespace ep {
