@@ -282,7 +282,7 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "fp8_e4m3 payload / bf16 combine, fp32 accumulate",
-        "data": "synthetic (seeded; page-3 score distribution, N(0,1) tokens and expert outputs)",
+        "data": "synthetic (seeded; the DeepEP routing study's score distribution, N(0,1) tokens and expert outputs)",
         "config": config,
         "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
@@ -502,7 +502,7 @@ def run_ht_backward(args, ep):
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "execution": args.mode,
         "ms_per_step_eager": round(ms_eager, 5), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16 gradients, fp32 accumulate",
-        "data": "synthetic (seeded; page-3 score distribution, N(0,1) gradients and expert outputs)",
+        "data": "synthetic (seeded; the DeepEP routing study's score distribution, N(0,1) gradients and expert outputs)",
         "config": {"workload": "ht_prefill_4096_backward", "tokens": n_tok, "hidden": H, "experts": E,
                    "top_k": K, "nodes": 8, "ranks_per_node": 8, "max_nodes_per_token": 4,
                    "rows": rows2, "algorithmic_bytes_per_step": total},

@@ -2,7 +2,7 @@
 alternative the DeepEP page's high-throughput traffic study compares).
 
 - The page's printed per-GPU copy counts: 6.26 cross-node copies per token
-  with the 4-node limit, 6.50 without (tests/golden/page3_routing_study.txt),
+  with the 4-node limit, 6.50 without (tests/golden/deepep_routing_study.txt),
   reproduced through the numpy restatement of the study; the oracle's row
   counts must equal that restatement's exact totals.
 - Brute force: every row recounted from its definition on small inputs.
@@ -20,7 +20,7 @@ import ep_inputs as I
 import oracle
 from oracle import page_sim
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page3_routing_study.txt")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "deepep_routing_study.txt")
 
 
 def _golden_per_gpu(key):

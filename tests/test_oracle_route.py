@@ -14,7 +14,7 @@ import ep_inputs as I
 import oracle
 from oracle import page_sim
 
-GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page3_routing_study.txt")
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "deepep_routing_study.txt")
 
 
 def _golden_rows():
