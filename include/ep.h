@@ -211,7 +211,10 @@ ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t *topk_idx,
                              ep_stream_t stream, ep_handle_t *out);
 
 /* Return the handle's storage to the group (NCCL-EP ncclEpHandleDestroy).
- * Stream-ordered reuse: work already enqueued with the handle may still run. */
+ * Stream-ordered reuse: work already enqueued with the handle may still run.
+ * The value must not be used afterwards: until a new handle takes the same
+ * slot, every call rejects it with EP_ERR_INVALID_ARGUMENT (as it rejects a
+ * pointer that is no handle at all); after that it names the new handle. */
 ep_status_t ep_destroy_handle(ep_handle_t handle);
 
 /* Rows received by `rank` (NCCL-EP ncclEpHandleGetNumRecvTokens).  BLOCKING:
