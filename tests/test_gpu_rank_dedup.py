@@ -28,7 +28,7 @@ def _bf16(a):
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
 
 
-def _run(w, weights, sample=None):
+def _run(w, weights, sample=None, fp8=True):
     """Route, handle and dispatch with the per-rank stage 2; compare maps,
     counts, rows and metadata with the oracle.  Returns (group, handle, topk,
     per-rank layout)."""
@@ -37,7 +37,7 @@ def _run(w, weights, sample=None):
     R = N * G
     scores = I.scores_for(w)
     x = I.tokens_for(w)
-    g = group_for(w, ht_stage2="rank")
+    g = group_for(w, ht_stage2="rank", payload="fp8" if fp8 else "bf16")
     try:
         topk_d = torch.empty((S * T, K), dtype=torch.int32, device="cuda")
         ep.ep_route(g, dev(scores), topk_d)
@@ -68,7 +68,7 @@ def _run(w, weights, sample=None):
         np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2_TOPK)[:rows2]), mt)
         np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2_WEIGHTS)[:rows2]), mw)
         toks = np.arange(S * T) if sample is None else sample
-        img = oracle.token_rows(I.bf16_bits(x)[toks], True)
+        img = oracle.token_rows(I.bf16_bits(x)[toks], fp8)
         st1, st2 = buffer(g, A.EP_BUF_HT_STAGE1), buffer(g, A.EP_BUF_HT_STAGE2)
         for j, i in enumerate(toks):
             r1 = lay1["node_row"][i][lay1["node_row"][i] >= 0]
@@ -105,6 +105,19 @@ def test_per_rank_dispatch_all_rows_and_combine():
         with pytest.raises(ep.EpError) as ei:
             ep.ep_combine_backward(h, out, dev(weights), _bf16(P))
         assert ei.value.status == A.EP_ERR_UNSUPPORTED
+        assert ep.ep_get_device_error(g) == 0
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_per_rank_bf16_payload():
+    """The per-rank stage 2 with BF16 rows (14336 bytes at hidden 7168): every
+    row, map and received top-k against the oracle."""
+    w = I.HT_PREFILL.with_(num_src_ranks=2, tokens_per_rank=150, seed=35)
+    say("HT per-rank stage 2, BF16 payload: S=2 T=150 H=7168 (all rows)")
+    g, h, topk, lay = _run(w, I.normal_weights(w.num_tokens, 8, 35), fp8=False)
+    try:
         assert ep.ep_get_device_error(g) == 0
         ep.ep_destroy_handle(h)
     finally:
