@@ -122,6 +122,7 @@ SIGNATURES = {
     "ep_get_buffer": (_S, [_P, ctypes.c_int32, _PT]),
     "ep_handle_get_buffer": (_S, [_P, ctypes.c_int32, _PT]),
     "ep_get_partition": (_S, [_P, ctypes.c_int32, ctypes.c_int32, _PT]),
+    "ep_quantize": (_S, [_P, _PT, _PT, _PT, _P]),
     "ep_combine": (_S, [_P, _PT, _PT, _PT, ctypes.c_int32, _P]),
     "ep_complete": (_S, [_P, _P]),
     "ep_combine_backward": (_S, [_P, _PT, _PT, _PT, _PT, _PT, _P]),

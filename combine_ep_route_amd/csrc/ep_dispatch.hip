@@ -384,6 +384,42 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
   }
 }
 
+// A3 on its own, for callers that keep FP8 tokens and dispatch them
+// pre-quantised: the same chunk mapping and quantize() as the dispatch, so
+// the codes and scales are the ones the dispatch would write.  Codes go out as 16-byte stores; each block's scale is stored by
+// the first lane of its 8.
+template <int NV>
+__global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a, int W) {
+  const int lane = threadIdx.x & 63;
+  const int C = a.H / 16;
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
+  const int64_t total = a.n * W;
+  for (int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); gw < total; gw += waves) {
+    const int64_t i = gw / W;
+    const int part = static_cast<int>(gw - i * W);
+    const int c0 = part * NV * 64 + lane;
+    Raw raw[NV];
+    const u32x4 zero{0, 0, 0, 0};
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = c0 + v * 64;
+      const u32x4* s4 = reinterpret_cast<const u32x4*>(a.x + i * a.ld_x + 16 * c);
+      raw[v].a = c < C ? s4[0] : zero;
+      raw[v].b = c < C ? s4[1] : zero;
+      raw[v].scale = 0.0f;
+    }
+#pragma unroll
+    for (int v = 0; v < NV; ++v) quantize(raw[v]);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = c0 + v * 64;
+      if (c >= C) continue;
+      store_nt(raw[v].a, a.q + i * a.ld_q + 16 * c);
+      if ((c & 7) == 0) __builtin_nontemporal_store(raw[v].scale, a.scales + i * a.ld_s + (c >> 3));
+    }
+  }
+}
+
 // Chunks per lane in one wave's share of a token: enough memory-level
 // parallelism per wave while keeping the wave's registers low enough for
 // full occupancy; a token spans W = ceil(C / (64*NV)) waves.
@@ -414,6 +450,16 @@ void launch_in(const DispatchArgs& p, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream) {
+  if (a.n == 0) return hipSuccess;
+  const int C = a.H / 16;
+  const int W = (C + 64 * kChunksPerLane - 1) / (64 * kChunksPerLane);
+  int64_t blocks = (a.n * W + 3) / 4;
+  if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
+  quantize_kernel<kChunksPerLane><<<dim3(static_cast<unsigned>(blocks)), dim3(256), 0, stream>>>(a, W);
+  return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const DispatchArgs& p, hipStream_t stream) {
   if (p.n == 0) return hipSuccess;

@@ -221,6 +221,20 @@ struct DispatchArgs {
 };
 hipError_t launch_dispatch(const DispatchArgs& a, hipStream_t stream);
 
+// FP8 quantisation alone: BF16 [n, H] -> codes [n, H] + scales [n, H/128],
+// the dispatch's own arithmetic (H % 128 == 0).
+struct QuantArgs {
+  const uint16_t* x;      // BF16 [n, H]
+  int64_t ld_x;           // elements
+  uint8_t* q;             // codes [n, H]
+  int64_t ld_q;           // bytes
+  float* scales;          // [n, H/128]
+  int64_t ld_s;           // elements
+  int64_t n;
+  int H;
+};
+hipError_t launch_quantize(const QuantArgs& a, hipStream_t stream);
+
 hipError_t launch_combine(const CombineArgs& a, hipStream_t stream);
 
 struct CombineBwdArgs {

@@ -680,6 +680,29 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   return EP_OK;
 }
 
+EP_API ep_status_t ep_quantize(ep_group_t group, const ep_tensor_t* tokens, ep_tensor_t* q, ep_tensor_t* scales,
+                               ep_stream_t stream) {
+  Group* g = reinterpret_cast<Group*>(group);
+  if (!group_ok(g) || !g->fp8) return EP_ERR_INVALID_ARGUMENT;
+  const int H = g->cfg.hidden;
+  if (!check2d(tokens, EP_DTYPE_BF16, -1, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
+  const int64_t n = tokens->sizes[0];
+  if (!check2d(q, EP_DTYPE_FP8_E4M3, n, H, EP_TAG_TOKENS, true)) return EP_ERR_INVALID_ARGUMENT;
+  if (!check2d(scales, EP_DTYPE_F32, n, H / 128, EP_TAG_SCALES, false)) return EP_ERR_INVALID_ARGUMENT;
+  const hipStream_t s = as_stream(stream);
+  if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
+  QuantArgs a{};
+  a.x = static_cast<const uint16_t*>(tokens->data);
+  a.ld_x = tokens->strides[0];
+  a.q = static_cast<uint8_t*>(q->data);
+  a.ld_q = q->strides[0];
+  a.scales = static_cast<float*>(scales->data);
+  a.ld_s = scales->strides[0];
+  a.n = n;
+  a.H = H;
+  return from_hip(launch_quantize(a, s));
+}
+
 namespace {
 ep_status_t buffer_view(Group* g, int32_t which, int ll_half, ep_tensor_t* view) {
   const bool ll = g->cfg.mode == EP_MODE_LL;

@@ -161,6 +161,13 @@ def ep_dispatch(handle: Handle, tokens: torch.Tensor, scales: Optional[torch.Ten
         handle._staged = (tokens, scales, topk_weights, recv_counts)   # alive until ep_complete
 
 
+def ep_quantize(group: Group, tokens: torch.Tensor, q: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    x = desc(tokens, A.EP_TAG_TOKENS)
+    qd = desc(q, A.EP_TAG_TOKENS)
+    sd = desc(scales, A.EP_TAG_SCALES)
+    _check("ep_quantize", A.lib().ep_quantize(group.ptr, _ref(x), _ref(qd), _ref(sd), _stream(stream)))
+
+
 def ep_combine(handle: Handle, expert_out: torch.Tensor, topk_weights: Optional[torch.Tensor],
                out: torch.Tensor, send_only: bool = False, stream=None) -> None:
     y = desc(expert_out, A.EP_TAG_TOKENS)

@@ -286,6 +286,23 @@ ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t *tokens,
                         ep_tensor_t *recv_counts, int32_t send_only,
                         ep_stream_t stream);
 
+/* FP8 E4M3 quantisation alone ("NVSHMEM and DeepEP", FP8 dispatch with one
+ * fp32 scale per 128 elements; "NCCL EP paper notes": quantisation is part of
+ * the send stage's preparation).  ep_dispatch quantises BF16 tokens itself;
+ * this call is for callers that want the FP8 tokens on their own, to keep
+ * them or to dispatch them more than once, passing them to ep_dispatch as
+ * pre-quantised tokens (tokens FP8, scales F32).  The codes and scales are
+ * the ones ep_dispatch writes when it quantises BF16 tokens itself:
+ * scale = amax/448 per 128-element block, codes the nearest-even,
+ * saturating E4M3 of x/scale; an all-zero block gets scale 0 and codes 0.
+ *   tokens: BF16 [n, H], rows 16-byte aligned, innermost contiguous.
+ *   q:      FP8_E4M3 [n, H] out, rows 16-byte aligned.
+ *   scales: F32 [n, H/128] out.
+ * Errors: EP_ERR_INVALID_ARGUMENT (a group whose payload is not FP8, or a
+ * descriptor that does not match). */
+ep_status_t ep_quantize(ep_group_t group, const ep_tensor_t *tokens, ep_tensor_t *q,
+                        ep_tensor_t *scales, ep_stream_t stream);
+
 /* Group-owned receive buffers, as U8/I32/F32 views (device memory).  Rows
  * and messages start on 128-byte boundaries: the U8 views' row stride
  * (strides[0]) is the row / message size rounded up to 128 bytes.  When H is
