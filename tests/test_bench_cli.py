@@ -1,0 +1,60 @@
+"""bench.py's contract on the host: one GPU only, no silent run without a GPU,
+the algorithmic byte counts of the measured workloads, and the stored PMC
+traffic readings."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args], capture_output=True,
+                          text=True, timeout=300, env=dict(os.environ, WORLD_SIZE="1"))
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="checks the no-GPU path")
+def test_no_gpu_is_an_error():
+    r = _run("--steps", "1", "--warmup", "0")
+    assert r.returncode == 2
+    assert "needs a GPU" in r.stderr
+
+
+def test_ht_step_bytes():
+    # 4096 tokens of the DeepEP routing study (seed 0): 16,248 stage-1 rows,
+    # 32,768 stage-2 rows; scores 4,194,304 + tokens 58,720,256 + topk and
+    # weights 262,144 + stage-1 rows and metadata 121,275,072 + stage-2 rows
+    # and metadata 242,614,272 + combine 528,744,448 bytes
+    ab = bench.algorithmic_bytes(4096, 8, 7168, 16248, 32768, 256)
+    assert ab["combine"] == 469_762_048 + 131_072 + 131_072 + 58_720_256
+    assert ab["dispatch"] == 58_720_256 + 262_144 + 16248 * (7392 + 72) + 32768 * (7392 + 12)
+    assert ab["total"] == 955_810_496
+    assert ab["total"] - ab["combine"] == 427_066_048          # the HT dispatch side, scores included
+
+
+def test_ll_step_bytes():
+    # 64 sources x 128 tokens: scores 8,388,608 + tokens 117,440,512 + topk and
+    # slot map 524,288 + counts 65,536 + messages 485,490,688 = 611,909,632 on
+    # the dispatch side
+    ab = bench.ll_algorithmic_bytes(8192, 8, 7168, 256, 64)
+    assert ab["total"] - ab["combine"] == 611_909_632
+    assert ab["total"] == 1_669_398_528
+    assert bench.ll_algorithmic_bytes(8192, 8, 7168, 256, 64, fp8=False)["total"] == 2_124_480_512
+
+
+def test_stored_traffic_is_consistent():
+    ab = bench.algorithmic_bytes(4096, 8, 7168, 16248, 32768, 256)
+    for kernel in ("dispatch", "combine"):
+        t = bench.stored_traffic(kernel)
+        if t is not None:       # only while the kernel sources match the profiled ones
+            assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
