@@ -213,19 +213,18 @@ def time_steps(step, args, stream, out_of, ep, g, n_calls=4):
             step(0)            # warm the capture stream
         torch.cuda.current_stream().wait_stream(cap)
         torch.cuda.synchronize()
+        # one graph of exactly `steps` steps (the input sets in turn), so the
+        # timed region is exactly that many steps
         with torch.cuda.graph(graph, stream=cap):
-            for j in range(N_SETS):
+            for j in range(args.steps):
                 step(j)
-        reps = max(1, args.steps // N_SETS)
-        for _ in range(3):
-            graph.replay()
+        graph.replay()             # untimed: the graph's first launch
         torch.cuda.synchronize()
-        log(f"[bench] graph: timing {reps * N_SETS} steps ({reps} replays)")
+        log(f"[bench] graph: timing {args.steps} steps (one replay)")
         t0 = time.perf_counter()
-        for _ in range(reps):
-            graph.replay()
+        graph.replay()
         torch.cuda.synchronize()
-        ms_per_step = (time.perf_counter() - t0) * 1e3 / (reps * N_SETS)
+        ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
         assert ep.ep_get_device_error(g) == 0
         ref = out_of(0).clone()
         step(0)
