@@ -227,8 +227,9 @@ __global__ __launch_bounds__(256) void layout_scan_ll_kernel(LayoutArgs a) {
       chunk_prefix(a.hist_e, 0, tps, 0, [=](int tt) { return static_cast<int64_t>(src * tps + tt) * E + e; });
 }
 
-// HT: one workgroup turns the tile histograms into exclusive prefix sums
-// (the kernel boundary makes the counts of every tile visible; no fences).
+// HT: two workgroups turn the tile histograms into exclusive prefix sums,
+// one for the stage-2 keys and one for the stage-1 ranks (the kernel
+// boundary makes the counts of every tile visible; no fences).
 __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
   extern __shared__ int smem[];
   const int B = blockDim.x;
@@ -257,12 +258,15 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     const int lane = tid & 63, wv = tid >> 6, nw = B >> 6;
 
     // Expert pair (e, c): tiles [c*cl_e, ...), address stride E.
-    const bool has_e = tid < ce * E;
+    // Workgroup 0 scans the stage-2 keys, workgroup 1 the stage-1 ranks:
+    // the two are independent, and split they run side by side.
+    const bool blk_e = blockIdx.x == 0, blk_r = blockIdx.x == 1;
+    const bool has_e = blk_e && tid < ce * E;
     const int e = tid % E, ce_i = tid / E;
     const int je0 = ce_i * cl_e, ne = has_e ? max(0, min(cl_e, n_tiles - je0)) : 0;
     int32_t* pe = a.hist_e + static_cast<int64_t>(je0) * E + e;
     // Rank pair (d, c): positions [c*cl_r, ...) of the rail sequence.
-    const bool has_r = tid < cr * R;
+    const bool has_r = blk_r && tid < cr * R;
     const int d = tid % R, cr_i = tid / R, n = d / G, g = d - (d / G) * G;
     const int nsrc = g < a.S ? (a.S - g + G - 1) / G : 0;
     const int pr0 = cr_i * cl_r, nr = has_r ? max(0, min(cl_r, nsrc * tps - pr0)) : 0;
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     // chunks, then one exclusive scan of the key totals across the
     // workgroup (shuffles inside a wave, one barrier across waves).
     int te = 0, tr = 0;
-    if (tid < E) {
+    if (blk_e && tid < E) {
       for (int c = 0; c < ce; ++c) {
         const int t = part_e[c * E + tid];
         part_e[c * E + tid] = te;
@@ -306,7 +310,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
       }
       a.c2[tid] = te;
     }
-    if (tid < R) {
+    if (blk_r && tid < R) {
       for (int c = 0; c < cr; ++c) {
         const int t = part_r[c * R + tid];
         part_r[c * R + tid] = tr;
@@ -324,11 +328,11 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     __syncthreads();
     int be = 0, br = 0;
     for (int q = 0; q < wv; ++q) { be += scratch[q]; br += scratch[nw + q]; }
-    if (tid < E) {
+    if (blk_e && tid < E) {
       tot_e[tid] = be + ie - te;
       a.off2[tid] = be + ie - te;
     }
-    if (tid < R) {
+    if (blk_r && tid < R) {
       tot_r[tid] = br + ir - tr;
       a.off1[tid] = br + ir - tr;
     }
@@ -443,7 +447,7 @@ hipError_t launch_layout(const LayoutArgs& a_in, hipStream_t stream) {
   else layout_count_kernel<32><<<grid, block, lds, stream>>>(a);
   if (a.ll_fused) return hipGetLastError();
   if (a.ht) {
-    layout_scan_kernel<<<dim3(1), dim3(kScanThreads), layout_scan_lds_bytes(a.E2, a.N, a.G, a.S, a.tps), stream>>>(a);
+    layout_scan_kernel<<<dim3(2), dim3(kScanThreads), layout_scan_lds_bytes(a.E2, a.N, a.G, a.S, a.tps), stream>>>(a);
   } else {
     const int64_t pairs = static_cast<int64_t>(a.E2) * a.S;
     layout_scan_ll_kernel<<<dim3(static_cast<unsigned>((pairs + 255) / 256)), dim3(256), 0, stream>>>(a);
