@@ -239,10 +239,12 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
   {
     // HT.  Keys: the E stage-2 keys (sequence: every tile in order) and the R
     // stage-1 ranks d = n*G + g (sequence: the tiles of the sources at
-    // position g, tps consecutive tiles per source).  A thread owns one
-    // (key, chunk) of each kind; it walks its chunk with pointer strides
-    // (no divisions in the loops) and keeps up to kScanRegs counts in
-    // registers between the sum and the rewrite.
+    // position g, tps consecutive tiles per source).  Workgroup 0 scans the
+    // stage-2 keys and workgroup 1 the stage-1 ranks: the two are
+    // independent, and split they run side by side.  A thread owns one
+    // (key, chunk) of its workgroup's kind; it walks its chunk with pointer
+    // strides (no divisions in the loops) and keeps up to kScanRegs counts
+    // in registers between the sum and the rewrite.
     const int G = a.G, R = N * G, tps = a.tps;
     // Chunks per key: enough for kScanRegs tiles each, at most B / keys.
     const int max_rail = ((a.S + G - 1) / G) * tps;
@@ -257,10 +259,8 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     int* scratch = tot_r + R;            // [2][B/64]
     const int lane = tid & 63, wv = tid >> 6, nw = B >> 6;
 
-    // Expert pair (e, c): tiles [c*cl_e, ...), address stride E.
-    // Workgroup 0 scans the stage-2 keys, workgroup 1 the stage-1 ranks:
-    // the two are independent, and split they run side by side.
     const bool blk_e = blockIdx.x == 0, blk_r = blockIdx.x == 1;
+    // Expert pair (e, c): tiles [c*cl_e, ...), address stride E.
     const bool has_e = blk_e && tid < ce * E;
     const int e = tid % E, ce_i = tid / E;
     const int je0 = ce_i * cl_e, ne = has_e ? max(0, min(cl_e, n_tiles - je0)) : 0;
@@ -298,8 +298,8 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     if (has_e) part_e[ce_i * E + e] = se;
     if (has_r) part_r[cr_i * R + d] = sr;
     __syncthreads();
-    // Thread x owns key x of each kind (E, R <= B): prefix over the key's
-    // chunks, then one exclusive scan of the key totals across the
+    // Thread x owns key x of its workgroup's kind (E, R <= B): prefix over
+    // the key's chunks, then one exclusive scan of the key totals across the
     // workgroup (shuffles inside a wave, one barrier across waves).
     int te = 0, tr = 0;
     if (blk_e && tid < E) {
