@@ -15,11 +15,17 @@ N(0,1) logits.  Four input sets rotate so that no step reads what the
 previous one left in the last-level cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--mode graph|eager]
+                    [--workload ht_prefill|ht_prefill_rank|ll_decode|ll_decode_1src|
+                                ll_decode_bf16|ht_backward]
 
 Prints one JSON line (rank 0).  value = algorithmic bytes of one step /
-step time, in GB/s; tokens/s and the fraction of the 8 TB/s HBM peak are
-reported beside it.  The roofline object describes the dominant kernel with
-its own average duration from HIP events recorded on the launch stream.
+step time, in GB/s, with the step time from one replay of a HIP graph that
+holds exactly K captured steps; tokens/s and the fraction of the 8 TB/s HBM
+peak are reported beside it.  The roofline object describes the dominant
+kernel with its own average duration from HIP events recorded on the launch
+stream.  The other workloads (LL decode, per-rank stage 2, backward) report
+the same fields for their own steps.
 """
 from __future__ import annotations
 
