@@ -40,9 +40,13 @@ _TORCH = {v: k for k, v in _DTYPES.items()}
 
 
 def desc(t: Optional[torch.Tensor], tag: int = A.EP_TAG_NONE):
-    """ep_tensor_t describing a torch tensor (None -> NULL)."""
+    """ep_tensor_t describing a torch tensor (None -> NULL).  Every tensor
+    the library reads or writes lives in device memory: a host tensor is
+    refused here, before its address could reach a kernel."""
     if t is None:
         return None
+    if not t.is_cuda:
+        raise ValueError(f"ep tensors must be on the GPU, got a {t.device} tensor")
     if t.dim() < 1 or t.dim() > 3:
         raise ValueError("ep tensors have 1 to 3 dimensions")
     d = A.EpTensor()

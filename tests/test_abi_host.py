@@ -271,3 +271,12 @@ def test_device_error_before_any_launch(host_group):
     code = ctypes.c_int32(99)
     assert A.lib().ep_get_device_error(host_group, ctypes.byref(code)) == A.EP_OK
     assert code.value == 0
+
+
+def test_binding_refuses_host_tensors():
+    """A host tensor's address must never reach a kernel: the binding
+    refuses it before calling the library."""
+    import torch
+    from combine_ep_route_amd import ep as binding
+    with pytest.raises(ValueError, match="on the GPU"):
+        binding.desc(torch.zeros((4, 8), dtype=torch.float32))
