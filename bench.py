@@ -16,8 +16,8 @@ previous one left in the last-level cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--mode graph|eager]
-                    [--workload ht_prefill|ht_prefill_rank|ll_decode|ll_decode_1src|
-                                ll_decode_bf16|ht_backward]
+                    [--workload ht_prefill|ht_prefill_rank|ht_prefill_nolimit|ll_decode|
+                                ll_decode_1src|ll_decode_bf16|ht_backward]
 
 Prints one JSON line (rank 0).  value = algorithmic bytes of one step /
 step time, in GB/s, with the step time from one replay of a HIP graph that
@@ -309,7 +309,7 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
     }
 
 
-def run_ht(args, ep, per_rank=False):
+def run_ht(args, ep, per_rank=False, node_limit=4):
     w = I.HT_PREFILL
     n_tok, E, K, H = w.num_tokens, w.num_experts, w.top_k, w.hidden
     log(f"[bench] building inputs: {n_tok} tokens, hidden {H}, {E} experts, top-{K}")
@@ -329,7 +329,7 @@ def run_ht(args, ep, per_rank=False):
     Y_d = Y.to(dev)
 
     g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
-                           max_nodes_per_token=4, hidden=H, max_tokens_per_rank=n_tok,
+                           max_nodes_per_token=node_limit, hidden=H, max_tokens_per_rank=n_tok,
                            num_src_ranks=1, payload="fp8", num_cus=args.num_cus,
                            ht_stage2="rank" if per_rank else "expert")
     stream = torch.cuda.current_stream()
@@ -362,16 +362,17 @@ def run_ht(args, ep, per_rank=False):
     ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank)
 
     mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
-    config = {"workload": "ht_prefill_4096_per_rank_plus_combine" if per_rank else "ht_prefill_4096_plus_combine",
+    name = "ht_prefill_4096" + ("_per_rank" if per_rank else "") + ("" if node_limit else "_no_node_limit")
+    config = {"workload": name + "_plus_combine",
               "tokens": n_tok, "hidden": H, "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
-              "max_nodes_per_token": 4, "stage2": "per_rank" if per_rank else "per_expert",
+              "max_nodes_per_token": node_limit, "stage2": "per_rank" if per_rank else "per_expert",
               "stage1_rows": rows1, "stage2_rows": rows2, "algorithmic_bytes_per_step": ab["total"]}
-    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=not per_rank,
-                         pct=pct)
+    result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
+                         traffic_ok=not per_rank and node_limit == 4, pct=pct)
     result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
         result["dtype"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
-    if not args.no_cpu_baseline and not per_rank:
+    if not args.no_cpu_baseline and not per_rank and node_limit == 4:
         log("[bench] timing the CPU oracle on the same workload")
         result["cpu_baseline"] = cpu_baseline(scores, x, weights, Y, n_tok)
     ep.ep_destroy_group(g)
@@ -538,14 +539,15 @@ def main(argv=None):
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
                          "eager: every step is enqueued from Python")
-    ap.add_argument("--workload", choices=["ht_prefill", "ht_prefill_rank", "ll_decode", "ll_decode_1src",
-                                           "ll_decode_bf16", "ht_backward"],
+    ap.add_argument("--workload", choices=["ht_prefill", "ht_prefill_rank", "ht_prefill_nolimit", "ll_decode",
+                                           "ll_decode_1src", "ll_decode_bf16", "ht_backward"],
                     default="ht_prefill",
                     help="ht_prefill: 4096 tokens, HT dispatch + combine (the headline); "
                          "ll_decode: 64 sources x 128 tokens, staged LL dispatch + combine; "
                          "ll_decode_1src: one source's 128 tokens; "
                          "ht_backward: the backward pass at the prefill shape on forward handles; "
                          "ht_prefill_rank: the prefill step with the per-rank stage 2; "
+                         "ht_prefill_nolimit: the prefill step routed without the node limit; "
                          "ll_decode_bf16: the 64 x 128 decode step with BF16 messages (14352 B)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
@@ -571,8 +573,9 @@ def main(argv=None):
 
     import combine_ep_route_amd as ep
 
-    if args.workload in ("ht_prefill", "ht_prefill_rank"):
-        result = run_ht(args, ep, per_rank=args.workload == "ht_prefill_rank")
+    if args.workload in ("ht_prefill", "ht_prefill_rank", "ht_prefill_nolimit"):
+        result = run_ht(args, ep, per_rank=args.workload == "ht_prefill_rank",
+                        node_limit=0 if args.workload == "ht_prefill_nolimit" else 4)
     elif args.workload == "ht_backward":
         result = run_ht_backward(args, ep)
     elif args.workload == "ll_decode_bf16":
