@@ -88,6 +88,11 @@ struct Group {
   bool dev_ready = false;
   int device = -1;
   int num_cu = 0;
+
+  // Pinned host memory for the blocking count queries, allocated at the
+  // first query (hipHostMalloc) and freed with the group.
+  int32_t* host_counts = nullptr;
+  size_t host_counts_len = 0;
 };
 
 struct Handle {

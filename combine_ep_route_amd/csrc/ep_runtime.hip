@@ -237,6 +237,26 @@ ep_status_t ensure_maps(Handle* h, hipStream_t stream) {
   return st;
 }
 
+// Copies `count` device int32 values to the group's pinned host buffer on
+// the handle's stream and waits for that stream (the blocking count
+// queries).  Returns the host copy through *out.
+ep_status_t read_counts(Handle* h, const int32_t* src, size_t count, const int32_t** out) {
+  Group* g = h->g;
+  if (g->host_counts_len < count) {
+    if (g->host_counts) EP_HIP(hipHostFree(g->host_counts));
+    g->host_counts = nullptr;
+    g->host_counts_len = 0;
+    void* p = nullptr;
+    EP_HIP(hipHostMalloc(&p, count * sizeof(int32_t), hipHostMallocDefault));
+    g->host_counts = static_cast<int32_t*>(p);
+    g->host_counts_len = count;
+  }
+  EP_HIP(hipMemcpyAsync(g->host_counts, src, count * sizeof(int32_t), hipMemcpyDeviceToHost, h->stream));
+  EP_HIP(hipStreamSynchronize(h->stream));
+  *out = g->host_counts;
+  return EP_OK;
+}
+
 }  // namespace
 }  // namespace ep
 
@@ -410,6 +430,7 @@ EP_API ep_status_t ep_destroy_group(ep_group_t group) {
   Group* g = reinterpret_cast<Group*>(group);
   if (!group_ok(g)) return EP_ERR_INVALID_ARGUMENT;
   if (g->dev_ready) (void)hipDeviceSynchronize();
+  if (g->host_counts) (void)hipHostFree(g->host_counts);
   free_all(g);
   for (Handle* h : g->handles) {
     h->magic = kDeadMagic;
@@ -553,9 +574,8 @@ EP_API ep_status_t ep_handle_get_num_recv(ep_handle_t handle, int32_t rank, int6
   const int E = g->cfg.num_experts, S = g->cfg.num_src_ranks, L = g->L;
   const bool ll = g->cfg.mode == EP_MODE_LL;
   const size_t count = ll ? static_cast<size_t>(E) * S : static_cast<size_t>(g->E2);
-  std::vector<int32_t> host(count);
-  EP_HIP(hipStreamSynchronize(h->stream));
-  EP_HIP(hipMemcpy(host.data(), ll ? h->ll_count : h->c2, count * sizeof(int32_t), hipMemcpyDeviceToHost));
+  const int32_t* host = nullptr;
+  if (const ep_status_t st = read_counts(h, ll ? h->ll_count : h->c2, count, &host); st != EP_OK) return st;
   int64_t total = 0;
   // The rank's keys: its experts, or with the per-rank stage 2 the rank itself.
   const int keys = ll ? E : g->E2;
@@ -761,13 +781,12 @@ EP_API ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t wh
     const bool stage1 = which >= EP_BUF_HT_STAGE1 && which <= EP_BUF_HT_STAGE1_WEIGHTS;
     const int keys = stage1 || g->s2_rank ? 1 : g->L;   // stage 2 per expert: the rank's L experts
     const int k0 = stage1 || g->s2_rank ? rank : rank * g->L;
-    std::vector<int32_t> c(static_cast<size_t>(keys));
-    int32_t off = 0;
-    EP_HIP(hipStreamSynchronize(h->stream));
-    EP_HIP(hipMemcpy(&off, (stage1 ? h->off1 : h->off2) + k0, sizeof(int32_t), hipMemcpyDeviceToHost));
-    EP_HIP(hipMemcpy(c.data(), (stage1 ? h->c1 : h->c2) + k0, keys * sizeof(int32_t), hipMemcpyDeviceToHost));
-    first = off;
-    for (int32_t v : c) count += v;
+    const int32_t* off = nullptr;
+    if (const ep_status_t st = read_counts(h, (stage1 ? h->off1 : h->off2) + k0, 1, &off); st != EP_OK) return st;
+    first = *off;
+    const int32_t* c = nullptr;
+    if (const ep_status_t st = read_counts(h, (stage1 ? h->c1 : h->c2) + k0, keys, &c); st != EP_OK) return st;
+    for (int q = 0; q < keys; ++q) count += c[q];
   }
   // Row `first` of the view starts strides[0] elements per row further in.
   full.data = static_cast<uint8_t*>(full.data) + first * full.strides[0] * dtype_size(full.dtype);
