@@ -13,6 +13,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -325,6 +326,14 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   g->rows1_max = g->n_max * nodes_per_token;
   g->rows2_max = g->n_max * K;
   const int64_t tps = (Tm + kLayoutTile - 1) / kLayoutTile;
+  // Slot, row and map indices are 32-bit on the device.
+  const int64_t kIndexMax = INT32_MAX;
+  if (g->n_max * std::max<int64_t>(K, N) > kIndexMax || g->rows2_max > kIndexMax ||
+      (cfg.mode == EP_MODE_LL && static_cast<int64_t>(E) * S * Tm > kIndexMax) ||
+      S * tps * std::max<int64_t>(E, N) > kIndexMax) {
+    delete g;
+    return EP_ERR_UNSUPPORTED;
+  }
   g->tiles_max = static_cast<int>(S * tps);
 
   ep_status_t st = EP_OK;

@@ -161,8 +161,9 @@ typedef struct ep_handle *ep_handle_t;
  * `stream` orders the initialisation.  On failure nothing stays allocated.
  * Errors: EP_ERR_INVALID_ARGUMENT (NULL pointers, inconsistent topology,
  * hidden not a multiple of 128 with FP8, only one allocator hook),
- * EP_ERR_UNSUPPORTED (E > 1024, K > 32, N > 64, hidden > 16384 or
- * num_src_ranks > R), EP_ERR_OUT_OF_MEMORY, EP_ERR_HIP. */
+ * EP_ERR_UNSUPPORTED (E > 1024, K > 32, N > 64, hidden > 16384,
+ * num_src_ranks > R, or more LL slots, HT rows or map entries than 32-bit
+ * indices address), EP_ERR_OUT_OF_MEMORY, EP_ERR_HIP. */
 ep_status_t ep_create_group(const ep_config_t *config, ep_stream_t stream,
                             ep_group_t *out);
 

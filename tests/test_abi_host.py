@@ -111,6 +111,12 @@ def test_invalid_config_rejected_before_hip(bad):
 @pytest.mark.parametrize("bad", [
     dict(num_experts=2048, num_nodes=8, ranks_per_node=8), dict(top_k=33, num_experts=256),
     dict(num_src_ranks=65), dict(hidden=16384 + 128), dict(max_handles=65),
+    # more LL slots (E * S * T_max) than 32-bit indices address
+    dict(mode=A.EP_MODE_LL, num_nodes=32, ranks_per_node=32, num_experts=1024, num_src_ranks=1024,
+         max_tokens_per_rank=4096),
+    # more HT stage-2 rows (S * T_max * K) than 32-bit indices address
+    dict(num_nodes=32, ranks_per_node=32, num_experts=1024, top_k=32, num_src_ranks=1024,
+         max_tokens_per_rank=1 << 17),
 ])
 def test_unsupported_config(bad):
     pool = HostPool()
