@@ -78,6 +78,15 @@ class EpTensor(ctypes.Structure):
     ]
 
 
+STAT_FIELDS = ("route_calls", "handles_created", "dispatch_calls", "combine_calls", "complete_calls",
+               "combine_backward_calls", "dispatch_backward_calls", "quantize_calls", "tokens_routed",
+               "tokens_dispatched", "tokens_combined")
+
+
+class EpStats(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int64) for name in STAT_FIELDS]
+
+
 ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
 FREE_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p)
 
@@ -113,6 +122,7 @@ SIGNATURES = {
     "ep_create_group": (_S, [ctypes.POINTER(EpConfig), _P, ctypes.POINTER(_P)]),
     "ep_destroy_group": (_S, [_P]),
     "ep_group_memory": (_S, [_P, ctypes.POINTER(ctypes.c_int64)]),
+    "ep_group_stats": (_S, [_P, ctypes.POINTER(EpStats)]),
     "ep_route": (_S, [_P, _PT, _PT, _P]),
     "ep_create_handle": (_S, [_P, _PT, _P, ctypes.POINTER(_P)]),
     "ep_destroy_handle": (_S, [_P]),

@@ -89,6 +89,8 @@ struct Group {
   int device = -1;
   int num_cu = 0;
 
+  ep_stats_t stats{};   // host-side call counters
+
   // Pinned host memory for the blocking count queries, allocated at the
   // first query (hipHostMalloc) and freed with the group.
   int32_t* host_counts = nullptr;

@@ -49,6 +49,13 @@ int log_level() {
 
 inline hipStream_t as_stream(ep_stream_t s) { return reinterpret_cast<hipStream_t>(s); }
 
+// One line per counted call with EP_LOG=2.
+void trace(const Group* g, const char* what, int64_t tokens) {
+  if (log_level() < 2) return;
+  std::fprintf(stderr, "[ep] %s %s tokens=%lld K=%d H=%d\n", what, g->cfg.mode == EP_MODE_LL ? "LL" : "HT",
+               static_cast<long long>(tokens), g->cfg.top_k, g->cfg.hidden);
+}
+
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -458,6 +465,13 @@ EP_API ep_status_t ep_group_memory(ep_group_t group, int64_t* bytes) {
   return EP_OK;
 }
 
+EP_API ep_status_t ep_group_stats(ep_group_t group, ep_stats_t* stats) {
+  Group* g = reinterpret_cast<Group*>(group);
+  if (!group_ok(g) || !stats) return EP_ERR_INVALID_ARGUMENT;
+  *stats = g->stats;
+  return EP_OK;
+}
+
 // ===========================================================================
 // Routing
 // ===========================================================================
@@ -483,7 +497,13 @@ EP_API ep_status_t ep_route(ep_group_t group, const ep_tensor_t* scores, ep_tens
   a.M = g->M;
   a.J = g->J;
   a.topk = static_cast<int32_t*>(topk_idx->data);
-  return from_hip(launch_route(a, s));
+  const ep_status_t st = from_hip(launch_route(a, s));
+  if (st == EP_OK) {
+    ++g->stats.route_calls;
+    g->stats.tokens_routed += n;
+    trace(g, "route", n);
+  }
+  return st;
 }
 
 // ===========================================================================
@@ -564,6 +584,8 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   h->in_use = true;
   h->magic = kHandleMagic;
   *out = reinterpret_cast<ep_handle_t>(h);
+  ++g->stats.handles_created;
+  trace(g, "create_handle", n);
   return EP_OK;
 }
 
@@ -691,6 +713,9 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
   p.m2_w = g->m2_w;
   if (const ep_status_t st = from_hip(launch_dispatch(p, s)); st != EP_OK) return st;
   h->maps_ready = true;
+  ++g->stats.dispatch_calls;
+  g->stats.tokens_dispatched += h->n;
+  trace(g, send_only ? "dispatch (send stage)" : "dispatch", h->n);
   if (ll) {
     h->ll_half = half;
     g->ll_next = (half + 1) % g->ll_nbuf;
@@ -729,7 +754,12 @@ EP_API ep_status_t ep_quantize(ep_group_t group, const ep_tensor_t* tokens, ep_t
   a.ld_s = scales->strides[0];
   a.n = n;
   a.H = H;
-  return from_hip(launch_quantize(a, s));
+  const ep_status_t st = from_hip(launch_quantize(a, s));
+  if (st == EP_OK) {
+    ++g->stats.quantize_calls;
+    trace(g, "quantize", n);
+  }
+  return st;
 }
 
 namespace {
@@ -846,9 +876,13 @@ EP_API ep_status_t ep_combine(ep_handle_t handle, const ep_tensor_t* expert_out,
     // The gather-reduce is the receive stage: it waits for ep_complete.
     h->pend = Handle::kPendCombine;
     h->pend_comb = a;
-    return EP_OK;
+  } else if (const ep_status_t st = from_hip(launch_combine(a, s)); st != EP_OK) {
+    return st;
   }
-  return from_hip(launch_combine(a, s));
+  ++g->stats.combine_calls;
+  g->stats.tokens_combined += h->n;
+  trace(g, send_only ? "combine (send stage)" : "combine", h->n);
+  return EP_OK;
 }
 
 // ===========================================================================
@@ -895,7 +929,12 @@ EP_API ep_status_t ep_combine_backward(ep_handle_t handle, const ep_tensor_t* gr
   a.H = H;
   a.max_blocks = dispatch_block_cap(g);
   a.err = g->err;
-  return from_hip(launch_combine_backward(a, s));
+  const ep_status_t st = from_hip(launch_combine_backward(a, s));
+  if (st == EP_OK) {
+    ++g->stats.combine_backward_calls;
+    trace(g, "combine_backward", h->n);
+  }
+  return st;
 }
 
 EP_API ep_status_t ep_dispatch_backward(ep_handle_t handle, const ep_tensor_t* grad_expert_in,
@@ -926,7 +965,12 @@ EP_API ep_status_t ep_dispatch_backward(ep_handle_t handle, const ep_tensor_t* g
   a.ld_out = grad_tokens->strides[0];
   a.max_blocks = dispatch_block_cap(g);
   a.err = g->err;
-  return from_hip(launch_combine(a, s));
+  const ep_status_t st = from_hip(launch_combine(a, s));
+  if (st == EP_OK) {
+    ++g->stats.dispatch_backward_calls;
+    trace(g, "dispatch_backward", h->n);
+  }
+  return st;
 }
 
 EP_API ep_status_t ep_complete(ep_handle_t handle, ep_stream_t stream) {
@@ -938,11 +982,18 @@ EP_API ep_status_t ep_complete(ep_handle_t handle, ep_stream_t stream) {
   h->stream = s;
   const int pend = h->pend;
   h->pend = Handle::kPendNone;
-  if (pend == Handle::kPendCombine) return from_hip(launch_combine(h->pend_comb, s));
-  if (h->pend_counts)
-    return from_hip(launch_recv_counts(h->ll_count, g->cfg.num_experts, g->cfg.num_src_ranks,
-                                       h->pend_per_expert, h->pend_counts, s));
-  return EP_OK;
+  ep_status_t st = EP_OK;
+  if (pend == Handle::kPendCombine)
+    st = from_hip(launch_combine(h->pend_comb, s));
+  else if (h->pend_counts)
+    st = from_hip(launch_recv_counts(h->ll_count, g->cfg.num_experts, g->cfg.num_src_ranks,
+                                     h->pend_per_expert, h->pend_counts, s));
+  if (st == EP_OK) {
+    ++g->stats.complete_calls;
+    trace(g, pend == Handle::kPendCombine ? "complete (combine receive stage)" : "complete (dispatch receive stage)",
+          h->n);
+  }
+  return st;
 }
 
 // ===========================================================================

@@ -84,6 +84,12 @@ class Group:
         return b.value
 
 
+def ep_group_stats(group: Group) -> dict:
+    st = A.EpStats()
+    _check("ep_group_stats", A.lib().ep_group_stats(group.ptr, ctypes.byref(st)))
+    return {name: getattr(st, name) for name in A.STAT_FIELDS}
+
+
 class Handle:
     def __init__(self, ptr: int, group: Group, num_tokens: int):
         self.ptr = ptr

@@ -174,6 +174,25 @@ ep_status_t ep_destroy_group(ep_group_t group);
 /* Bytes of device memory the group holds. */
 ep_status_t ep_group_memory(ep_group_t group, int64_t *bytes);
 
+/* Host-side counters of the group's calls that returned EP_OK (a staged
+ * dispatch or combine counts when enqueued; its receive stage counts under
+ * complete_calls).  Nothing here reads the device.  With the environment
+ * variable EP_LOG=2 each counted call also prints one line to stderr. */
+typedef struct {
+    int64_t route_calls;
+    int64_t handles_created;
+    int64_t dispatch_calls;
+    int64_t combine_calls;
+    int64_t complete_calls;
+    int64_t combine_backward_calls;
+    int64_t dispatch_backward_calls;
+    int64_t quantize_calls;
+    int64_t tokens_routed;      /* rows of scores routed                  */
+    int64_t tokens_dispatched;  /* tokens of the handles dispatched       */
+    int64_t tokens_combined;    /* tokens of the handles combined         */
+} ep_stats_t;
+ep_status_t ep_group_stats(ep_group_t group, ep_stats_t *stats);
+
 /* ----------------------------------------------------------------------- */
 /* Routing (A1)                                                              */
 /* ----------------------------------------------------------------------- */

@@ -286,3 +286,21 @@ def test_binding_refuses_host_tensors():
     from combine_ep_route_amd import ep as binding
     with pytest.raises(ValueError, match="on the GPU"):
         binding.desc(torch.zeros((4, 8), dtype=torch.float32))
+
+
+def test_stats_start_at_zero_without_hip():
+    """A group made with allocator hooks (no HIP call) reports zero counters,
+    and the stats struct has the header's layout."""
+    import re as _re
+    src = open(HEADER).read()
+    body = _re.search(r"typedef struct \{(.*?)\} ep_stats_t;", src, _re.S).group(1)
+    names = _re.findall(r"int64_t\s+(\w+);", body)
+    assert tuple(names) == A.STAT_FIELDS
+    pool = HostPool()
+    st, g = _create(_cfg(pool))
+    assert st == A.EP_OK
+    out = A.EpStats()
+    assert A.lib().ep_group_stats(g, ctypes.byref(out)) == A.EP_OK
+    assert all(getattr(out, n) == 0 for n in A.STAT_FIELDS)
+    assert A.lib().ep_group_stats(None, ctypes.byref(out)) == A.EP_ERR_INVALID_ARGUMENT
+    assert A.lib().ep_destroy_group(g) == A.EP_OK
