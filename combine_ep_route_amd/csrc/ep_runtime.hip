@@ -668,18 +668,31 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
                        !contiguous2d(topk_weights)))
     return EP_ERR_INVALID_ARGUMENT;
   int per_expert = 0;
+  const bool counts_on_host = recv_counts && recv_counts->tag == EP_TAG_RECV_EXPERT_COUNTER_HOST;
   if (recv_counts) {
+    const int32_t tag = counts_on_host ? EP_TAG_RECV_EXPERT_COUNTER_HOST : EP_TAG_TOKENS_PER_EXPERT;
     const bool one_d = recv_counts->dtype == EP_DTYPE_I32 && recv_counts->ndim == 1 &&
                        recv_counts->sizes[0] == (ll ? E : g->E2) && recv_counts->strides[0] == 1 && recv_counts->data &&
-                       (recv_counts->tag == EP_TAG_NONE || recv_counts->tag == EP_TAG_TOKENS_PER_EXPERT);
-    const bool two_d = ll && recv_counts->ndim == 2 &&
-                       check2d(recv_counts, EP_DTYPE_I32, E, S, EP_TAG_TOKENS_PER_EXPERT, false) &&
+                       (recv_counts->tag == EP_TAG_NONE || recv_counts->tag == tag);
+    const bool two_d = ll && recv_counts->ndim == 2 && check2d(recv_counts, EP_DTYPE_I32, E, S, tag, false) &&
                        contiguous2d(recv_counts);
     if (!one_d && !two_d) return EP_ERR_INVALID_ARGUMENT;
     per_expert = ll && one_d;
   }
   if (send_only && !ll) return EP_ERR_UNSUPPORTED;
   if (h->pend != Handle::kPendNone) return EP_ERR_INVALID_ARGUMENT;   // complete the staged one first
+  int32_t* counts_out = recv_counts ? static_cast<int32_t*>(recv_counts->data) : nullptr;
+  if (counts_on_host) {
+    // The host counter must be pinned memory the device can write; the
+    // receive stage writes through its device address.
+    hipPointerAttribute_t attr{};
+    if (hipPointerGetAttributes(&attr, counts_out) != hipSuccess || attr.type != hipMemoryTypeHost ||
+        !attr.devicePointer) {
+      (void)hipGetLastError();
+      return EP_ERR_INVALID_ARGUMENT;
+    }
+    counts_out = static_cast<int32_t*>(attr.devicePointer);
+  }
   const hipStream_t s = as_stream(stream);
   if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
   h->stream = s;
@@ -720,7 +733,6 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
     h->ll_half = half;
     g->ll_next = (half + 1) % g->ll_nbuf;
   }
-  int32_t* counts_out = recv_counts ? static_cast<int32_t*>(recv_counts->data) : nullptr;
   if (send_only) {
     // The receive stage waits for ep_complete.
     h->pend = Handle::kPendDispatch;

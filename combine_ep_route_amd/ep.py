@@ -45,8 +45,9 @@ def desc(t: Optional[torch.Tensor], tag: int = A.EP_TAG_NONE):
     refused here, before its address could reach a kernel."""
     if t is None:
         return None
-    if not t.is_cuda:
-        raise ValueError(f"ep tensors must be on the GPU, got a {t.device} tensor")
+    if not t.is_cuda and not (tag == A.EP_TAG_RECV_EXPERT_COUNTER_HOST and t.is_pinned()):
+        raise ValueError(f"ep tensors must be on the GPU (or, for a host receive counter, pinned), "
+                         f"got a {t.device} tensor")
     if t.dim() < 1 or t.dim() > 3:
         raise ValueError("ep tensors have 1 to 3 dimensions")
     d = A.EpTensor()
@@ -164,7 +165,9 @@ def ep_dispatch(handle: Handle, tokens: torch.Tensor, scales: Optional[torch.Ten
     x = desc(tokens, A.EP_TAG_TOKENS)
     sc = desc(scales, A.EP_TAG_SCALES)
     w = desc(topk_weights, A.EP_TAG_TOPK_WEIGHTS)
-    rc = desc(recv_counts, A.EP_TAG_TOKENS_PER_EXPERT)
+    # a pinned host tensor is NCCL-EP's host-side receive counter
+    rc = desc(recv_counts, A.EP_TAG_TOKENS_PER_EXPERT if recv_counts is None or recv_counts.is_cuda
+              else A.EP_TAG_RECV_EXPERT_COUNTER_HOST)
     _check("ep_dispatch", A.lib().ep_dispatch(handle.ptr, _ref(x), _ref(sc), _ref(w), _ref(rc),
                                               int(bool(send_only)), _stream(stream)))
     if send_only:

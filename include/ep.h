@@ -286,7 +286,13 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  *            metadata.  Ignored in LL.
  *   recv_counts  : optional I32 out, tag TOKENS_PER_EXPERT: LL [E, S]
  *            counts per (expert, source) or [E] tokens per expert; HT [E]
- *            stage-2 rows per expert (PER_RANK: [R] rows per rank).
+ *            stage-2 rows per expert (PER_RANK: [R] rows per rank).  With
+ *            tag RECV_EXPERT_COUNTER_HOST (NCCL-EP's host-side receive
+ *            counter) data is pinned host memory (hipHostMalloc, or a
+ *            registered-at-allocation pinned buffer) that the receive stage
+ *            writes directly: once the stream reaches that point the counts
+ *            are on the host with no copy.  Pageable host memory is
+ *            rejected with EP_ERR_INVALID_ARGUMENT.
  *   send_only : 0, or (LL) enqueue the send stage only; HT returns
  *            EP_ERR_UNSUPPORTED (the staged mode is an LL feature).
  * With an FP8 payload each 128-element block is quantised as
