@@ -206,9 +206,10 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
   // Rows end on whole 128-byte lines when the scale bytes (H/32) are whole
   // 16-byte groups, so the LL header is 16-byte aligned: H % 512 == 0.
   const bool line_tail = (p.H & 511) == 0;
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * 4;
+  const int wpb = blockDim.x >> 6;                 // waves per workgroup
+  const int64_t waves = static_cast<int64_t>(gridDim.x) * wpb;
   const int64_t total = p.n * W;
-  for (int64_t gw = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6); gw < total; gw += waves) {
+  for (int64_t gw = static_cast<int64_t>(blockIdx.x) * wpb + (threadIdx.x >> 6); gw < total; gw += waves) {
     const int64_t i = gw / W;                       // token
     const int part = static_cast<int>(gw - i * W);  // which chunk range of it
     const int c0 = part * NV * 64 + lane;           // this lane's first chunk
@@ -425,14 +426,23 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a, int W) {
 // full occupancy; a token spans W = ceil(C / (64*NV)) waves.
 constexpr int kChunksPerLane = 4;
 
+// Waves per workgroup (every wave works on its own): 4 for HT and 2 for LL
+// were the fastest of 1, 2, 4 and 8 on the 4096-token prefill and the
+// 64 x 128-token decode dispatch.
+constexpr int kHtWavesPerGroup = 4;
+constexpr int kLlWavesPerGroup = 2;
+
 template <int IN, bool PAYLOAD, int KMAX, int NV>
 void launch_nv(const DispatchArgs& p, hipStream_t stream) {
   const int C = IN == 1 ? p.H / 8 : p.H / 16;
   const int W = PAYLOAD ? (C + 64 * NV - 1) / (64 * NV) : 1;
-  int64_t blocks = (p.n * W + 3) / 4;
-  if (p.max_blocks > 0 && blocks > p.max_blocks) blocks = p.max_blocks;
+  const int wpb = p.ht ? kHtWavesPerGroup : kLlWavesPerGroup;
+  int64_t blocks = (p.n * W + wpb - 1) / wpb;
+  // The CU cap counts 4-wave workgroups: smaller ones get as many waves.
+  const int64_t cap = static_cast<int64_t>(p.max_blocks) * 4 / wpb;
+  if (cap > 0 && blocks > cap) blocks = cap;
   if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
-  const dim3 grid(static_cast<unsigned>(blocks)), block(256);
+  const dim3 grid(static_cast<unsigned>(blocks)), block(64 * wpb);
   if (p.ht) dispatch_kernel<IN, true, PAYLOAD, KMAX, NV><<<grid, block, 0, stream>>>(p, W);
   else dispatch_kernel<IN, false, PAYLOAD, KMAX, NV><<<grid, block, 0, stream>>>(p, W);
 }

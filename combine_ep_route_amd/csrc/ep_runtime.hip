@@ -165,7 +165,7 @@ void fill_view(ep_tensor_t* v, void* data, int32_t dtype, int64_t d0, int64_t d1
 }
 
 int dispatch_block_cap(const Group* g) {
-  // One workgroup per token by default; with a CU cap, 4 per allowed CU.
+  // No cap by default; with a CU cap, four 4-wave workgroups per allowed CU.
   return g->cfg.num_cus > 0 ? g->cfg.num_cus * 4 : 0;
 }
 
