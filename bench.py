@@ -17,7 +17,7 @@ previous one left in the last-level cache.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--mode graph|eager]
                     [--workload ht_prefill|ht_prefill_rank|ht_prefill_nolimit|ll_decode|
-                                ll_decode_1src|ll_decode_bf16|ht_backward]
+                                ll_decode_1src|ll_decode_bf16|ht_backward|round_trip]
 
 Prints one JSON line (rank 0).  value = algorithmic bytes of one step /
 step time, in GB/s, with the step time from one replay of a HIP graph that
@@ -114,27 +114,35 @@ MIN_CPU_SECONDS = 10.0   # the oracle runs at least this long (whole runs)
 
 
 def cpu_baseline(scores, x, weights, Y, n_tok):
-    """The oracle on the same workload (all 4096 tokens), single thread,
-    repeated whole until MIN_CPU_SECONDS have passed."""
+    """The oracle on the same workload (all n_tok tokens), single thread,
+    repeated whole until MIN_CPU_SECONDS have passed.  Y None: the combine
+    takes the identity expert's output of the oracle's own stage-2 rows,
+    which is made outside the timed parts, as on the GPU."""
     import oracle
     xb = I.bf16_bits(x)
-    yb = I.bf16_bits(Y)
-    runs = 0
-    t0 = time.perf_counter()
+    yb = None if Y is None else I.bf16_bits(Y)
+    runs, busy = 0, 0.0
     while True:
+        t0 = time.perf_counter()
         topk = oracle.route(scores, 8, 8, 4)
         lay = oracle.layout_ht(topk, 1, 256, 8, 8)
         rows1, rows2 = int(lay["c1"].sum()), int(lay["c2"].sum())
-        oracle.pack_ht(xb, topk, weights, n_tok, 8, True, lay["node_row"], lay["row2"], rows1, rows2)
-        oracle.combine(yb, weights, lay["row2"])
+        pk = oracle.pack_ht(xb, topk, weights, n_tok, 8, True, lay["node_row"], lay["row2"], rows1, rows2)
+        t1 = time.perf_counter()
+        y = oracle.dequant_rows(pk["stage2"], 7168, True) if Y is None else yb
+        del pk
+        t2 = time.perf_counter()
+        oracle.combine(y, weights, lay["row2"])
+        busy += (t1 - t0) + (time.perf_counter() - t2)
         runs += 1
-        if time.perf_counter() - t0 >= MIN_CPU_SECONDS:
+        if busy >= MIN_CPU_SECONDS:
             break
-    dt = (time.perf_counter() - t0) / runs
+    dt = busy / runs
     b = algorithmic_bytes(n_tok, 8, 7168, rows1, rows2, 256)["total"]
+    expert = " (identity expert untimed)" if Y is None else ""
     return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
                 sample=f"the whole step workload ({n_tok} tokens: route, layout, FP8 quantise + HT pack, "
-                       f"combine), run {runs} times, {dt:.2f} s per run single-threaded",
+                       f"combine{expert}), run {runs} times, {dt:.2f} s per run single-threaded",
                 seconds=round(dt, 3), runs=runs, tokens_per_s=round(n_tok / dt, 1))
 
 
@@ -309,14 +317,19 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
     }
 
 
-def run_ht(args, ep, per_rank=False, node_limit=4):
-    w = I.HT_PREFILL
+def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
+    """HT dispatch + combine.  At the prefill shape the combine reads N(0,1)
+    expert outputs; the round trip (16384 tokens, Zipf popularity) combines
+    the identity expert's output of the dispatched stage-2 rows, made once
+    before the timed steps (every step routes the same scores)."""
+    round_trip = w is I.ROUND_TRIP
     n_tok, E, K, H = w.num_tokens, w.num_experts, w.top_k, w.hidden
-    log(f"[bench] building inputs: {n_tok} tokens, hidden {H}, {E} experts, top-{K}")
+    log(f"[bench] building inputs: {n_tok} tokens, hidden {H}, {E} experts, top-{K}, {w.scores} scores")
     scores = I.scores_for(w)
     x = I.tokens_for(w)
     weights = I.normal_weights(n_tok, K, w.seed)
-    Y = I.normal_bf16(n_tok * K, H, I.COMBINE.seed)   # (per rank: the first rows2 are used)
+    # (per rank: the first rows2 are used)
+    Y = None if round_trip else I.normal_bf16(n_tok * K, H, I.COMBINE.seed)
 
     dev = torch.device("cuda")
     sets = []
@@ -326,7 +339,7 @@ def run_ht(args, ep, per_rank=False, node_limit=4):
                          topk=torch.empty((n_tok, K), dtype=torch.int32, device=dev),
                          out=torch.empty((n_tok, H), dtype=torch.bfloat16, device=dev)))
     w_d = torch.from_numpy(weights).to(dev)
-    Y_d = Y.to(dev)
+    Y_d = None if Y is None else Y.to(dev)
 
     g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
                            max_nodes_per_token=node_limit, hidden=H, max_tokens_per_rank=n_tok,
@@ -358,21 +371,41 @@ def run_ht(args, ep, per_rank=False, node_limit=4):
     h = ep.ep_create_handle(g, sets[0]["topk"])
     rows2 = ep.ep_handle_get_num_recv(h, -1)
     rows1 = int(ep.ep_handle_get_map(h, ep._abi.EP_MAP_HT_RANK_COUNT).sum().item())
+    if round_trip:
+        # the identity expert: dequantised stage-2 rows, the combine's input
+        log(f"[bench] identity expert on {rows2} stage-2 rows (untimed)")
+        ep.ep_dispatch(h, sets[0]["x"], topk_weights=w_d)
+        Y_d = torch.empty((rows2, H), dtype=torch.bfloat16, device=dev)
+        ep.ep_dequantize_rows(g, ep.ep_get_buffer(g, ep._abi.EP_BUF_HT_STAGE2)[:rows2], Y_d)
     ep.ep_destroy_handle(h)
     ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank)
 
     mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
-    name = "ht_prefill_4096" + ("_per_rank" if per_rank else "") + ("" if node_limit else "_no_node_limit")
+    if round_trip:
+        name = f"ht_round_trip_{n_tok}_zipf"
+    else:
+        name = f"ht_prefill_{n_tok}" + ("_per_rank" if per_rank else "") + ("" if node_limit else "_no_node_limit")
     config = {"workload": name + "_plus_combine",
               "tokens": n_tok, "hidden": H, "experts": E, "top_k": K, "nodes": 8, "ranks_per_node": 8,
               "max_nodes_per_token": node_limit, "stage2": "per_rank" if per_rank else "per_expert",
               "stage1_rows": rows1, "stage2_rows": rows2, "algorithmic_bytes_per_step": ab["total"]}
+    headline = not per_rank and node_limit == 4 and not round_trip
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
-                         traffic_ok=not per_rank and node_limit == 4, pct=pct)
+                         traffic_ok=headline, pct=pct)
     result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
         result["dtype"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
-    if not args.no_cpu_baseline and not per_rank and node_limit == 4:
+    if round_trip:
+        result["data"] = ("synthetic (seeded; U[0,1) scores plus a normalised Zipf(1.1) expert popularity, "
+                          "N(0,1) tokens; the combine input is the identity expert's output of the "
+                          "dispatched rows, made once outside the timed steps)")
+        # end to end: the round trip returns every token within FP8 error of itself
+        xs, out = sets[0]["x"].float(), sets[0]["out"].float()
+        amax = xs.abs().view(n_tok, H // 128, 128).amax(dim=2, keepdim=True).expand(-1, -1, 128).reshape(n_tok, H)
+        bound = 2.0**-4 * xs.abs() + 2.0**-8 * xs.abs() + amax * 2.0**-9 + 1e-6
+        result["round_trip_within_fp8_bound"] = bool(((out - xs).abs() <= bound).all().item())
+        del xs, out, amax, bound
+    if not args.no_cpu_baseline and (headline or round_trip):
         log("[bench] timing the CPU oracle on the same workload")
         result["cpu_baseline"] = cpu_baseline(scores, x, weights, Y, n_tok)
     ep.ep_destroy_group(g)
@@ -540,7 +573,7 @@ def main(argv=None):
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
                          "eager: every step is enqueued from Python")
     ap.add_argument("--workload", choices=["ht_prefill", "ht_prefill_rank", "ht_prefill_nolimit", "ll_decode",
-                                           "ll_decode_1src", "ll_decode_bf16", "ht_backward"],
+                                           "ll_decode_1src", "ll_decode_bf16", "ht_backward", "round_trip"],
                     default="ht_prefill",
                     help="ht_prefill: 4096 tokens, HT dispatch + combine (the headline); "
                          "ll_decode: 64 sources x 128 tokens, staged LL dispatch + combine; "
@@ -548,7 +581,9 @@ def main(argv=None):
                          "ht_backward: the backward pass at the prefill shape on forward handles; "
                          "ht_prefill_rank: the prefill step with the per-rank stage 2; "
                          "ht_prefill_nolimit: the prefill step routed without the node limit; "
-                         "ll_decode_bf16: the 64 x 128 decode step with BF16 messages (14352 B)")
+                         "ll_decode_bf16: the 64 x 128 decode step with BF16 messages (14352 B); "
+                         "round_trip: 16384 tokens with Zipf(1.1) expert popularity, FP8 dispatch + "
+                         "combine of the identity expert's output")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters), then exit")
@@ -576,6 +611,8 @@ def main(argv=None):
     if args.workload in ("ht_prefill", "ht_prefill_rank", "ht_prefill_nolimit"):
         result = run_ht(args, ep, per_rank=args.workload == "ht_prefill_rank",
                         node_limit=0 if args.workload == "ht_prefill_nolimit" else 4)
+    elif args.workload == "round_trip":
+        result = run_ht(args, ep, w=I.ROUND_TRIP)
     elif args.workload == "ht_backward":
         result = run_ht_backward(args, ep)
     elif args.workload == "ll_decode_bf16":

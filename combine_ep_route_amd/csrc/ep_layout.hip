@@ -68,10 +68,23 @@ struct Entries {
 
 constexpr int kScanRegs = 16;      // tile counts a scan thread keeps in registers
 
-// Exclusive-prefix rewrite of values at idx(pos), pos in [p0, p1), 16
-// independent loads at a time so that the chain costs one round trip per 16
-// tiles instead of one per tile.
+// Sum, and exclusive-prefix rewrite, of the values at idx(pos), pos in
+// [p0, p1), 16 independent loads at a time so that the chain costs one
+// round trip per 16 tiles instead of one per tile.
 constexpr int kBatch = 16;
+
+template <class Idx>
+__device__ __forceinline__ int chunk_sum(const int32_t* base, int p0, int p1, Idx idx) {
+  int run = 0;
+  for (int pos = p0; pos < p1; pos += kBatch) {
+    int v[kBatch];
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) v[q] = pos + q < p1 ? base[idx(pos + q)] : 0;
+#pragma unroll
+    for (int q = 0; q < kBatch; ++q) run += v[q];
+  }
+  return run;
+}
 
 template <class Idx>
 __device__ __forceinline__ int chunk_prefix(int32_t* base, int p0, int p1, int run, Idx idx) {
@@ -273,7 +286,14 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
     // the first tile of the chunk: source g + (pr0/tps)*G, tile pr0 % tps
     const int r_src0 = g + (pr0 / tps) * G, r_tt0 = pr0 % tps;
 
-    const bool regs = cl_e <= kScanRegs && cl_r <= kScanRegs;
+    // Registers when the workgroup's chunks fit them; longer chunks (many
+    // tiles per key) go through memory in batches of kBatch loads.
+    const bool regs = blk_e ? cl_e <= kScanRegs : cl_r <= kScanRegs;
+    // tile counter of rail position pos of rank d: source g + (pos/tps)*G, tile pos % tps
+    auto rail = [=](int pos) {
+      return static_cast<int64_t>((g + (pos / tps) * G) * tps + pos % tps) * N + n;
+    };
+    auto expert = [=](int q) { return static_cast<int64_t>(q) * E; };
     int ve[kScanRegs], vr[kScanRegs];
     int se = 0, sr = 0;
     if (regs) {
@@ -288,12 +308,8 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
 #pragma unroll
       for (int q = 0; q < kScanRegs; ++q) { se += ve[q]; sr += vr[q]; }
     } else {
-      for (int q = 0; q < ne; ++q) se += pe[static_cast<int64_t>(q) * E];
-      int src = r_src0, tt = r_tt0;
-      for (int q = 0; q < nr; ++q) {
-        sr += a.hist_n[static_cast<int64_t>(src * tps + tt) * N + n];
-        if (++tt == tps) { tt = 0; src += G; }
-      }
+      se = chunk_sum(pe, 0, ne, expert);
+      sr = chunk_sum(a.hist_n, pr0, pr0 + nr, rail);
     }
     if (has_e) part_e[ce_i * E + e] = se;
     if (has_r) part_r[cr_i * R + d] = sr;
@@ -346,11 +362,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
           run += ve[q];
         }
       } else {
-        for (int q = 0; q < ne; ++q) {
-          const int h = pe[static_cast<int64_t>(q) * E];
-          pe[static_cast<int64_t>(q) * E] = run;
-          run += h;
-        }
+        chunk_prefix(pe, 0, ne, run, expert);
       }
     }
     if (has_r) {
@@ -364,13 +376,7 @@ __global__ __launch_bounds__(1024) void layout_scan_kernel(LayoutArgs a) {
           if (++tt == tps) { tt = 0; src += G; }
         }
       } else {
-        for (int q = 0; q < nr; ++q) {
-          int32_t* p = a.hist_n + static_cast<int64_t>(src * tps + tt) * N + n;
-          const int h = *p;
-          *p = run;
-          run += h;
-          if (++tt == tps) { tt = 0; src += G; }
-        }
+        chunk_prefix(a.hist_n, pr0, pr0 + nr, run, rail);
       }
     }
   }

@@ -178,6 +178,10 @@ def test_layout_ht_full_workloads(wname):
 @pytest.mark.parametrize("S,T,E,N,G,K", [
     (4, 32, 16, 2, 2, 2), (3, 600, 256, 8, 8, 8), (8, 77, 64, 4, 2, 5), (1, 1, 256, 8, 8, 8),
     (16, 300, 128, 4, 4, 16),
+    # chunks longer than a scan thread's registers hold, with ragged last batches:
+    # 129 tiles of one source (experts), 400 tiles over rails of two sources
+    # (1024 ranks and 1024 experts), experts long while ranks fit registers
+    (1, 8229, 256, 8, 8, 8), (40, 600, 1024, 32, 32, 8), (20, 900, 64, 4, 8, 5),
 ])
 def test_layout_ht_shapes(S, T, E, N, G, K):
     say(f"layout HT S={S} T={T} E={E} N={N} G={G} K={K}")
