@@ -11,6 +11,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 
@@ -39,6 +40,21 @@ def test_library_exports_every_declared_symbol():
     exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
     ep_syms = {s for s in exported if s.startswith("ep_")}
     assert ep_syms == set(_declared())
+
+
+def test_missing_library_is_an_error():
+    """Without the built library the binding raises: there is no fallback path."""
+    code = ("import combine_ep_route_amd._abi as A, combine_ep_route_amd as ep\n"
+            "A.LIB_PATH = '/nonexistent/libep.so'; A._lib = None\n"
+            "try:\n"
+            "    ep.ep_create_group(mode='ht', num_nodes=2, ranks_per_node=2, num_experts=16, top_k=2,\n"
+            "                       max_nodes_per_token=0, hidden=128, max_tokens_per_rank=8, num_src_ranks=1)\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                       cwd=ROOT, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "no fallback" in r.stdout
 
 
 def test_status_strings():
