@@ -590,7 +590,7 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
-              "multi-GPU runs are not part of this build", file=sys.stderr)
+              "it has no multi-GPU mode", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)

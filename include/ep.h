@@ -49,7 +49,7 @@ typedef enum {
     EP_ERR_OUT_OF_MEMORY = 3,    /* device allocation (or alloc_fn) failed    */
     EP_ERR_HIP = 4,              /* a HIP runtime call failed; see
                                     ep_last_hip_error()                      */
-    EP_ERR_UNSUPPORTED = 5       /* valid but outside this build's limits     */
+    EP_ERR_UNSUPPORTED = 5       /* valid but outside the library's limits    */
 } ep_status_t;
 
 /* Algorithm mode, chosen once at group creation (NCCL-EP: the group's
