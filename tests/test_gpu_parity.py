@@ -3,8 +3,9 @@
 Bit-exact for routing, counts, offsets, slot and row maps, FP8 codes, scales,
 headers and metadata; the combine is compared bit for bit as well (the
 stated tolerance, 1e-3 relative per element, is checked alongside and is
-implied by equality).  Full-size workloads compare everything the oracle can
-produce quickly and sample the rest (the rows of a few hundred tokens).
+implied by equality).  Full-size workloads are compared whole: every row,
+message and output token of the HT prefill, LL decode, combine and 16384-token
+round-trip workloads.
 """
 import numpy as np
 import pytest
@@ -270,11 +271,11 @@ def test_ll_dispatch_ragged_hidden():
 
 
 def test_ll_dispatch_full_decode_shape():
-    """64 sources x 128 tokens, hidden 7168, 8x8 ranks, node-limited top-8."""
+    """64 sources x 128 tokens, hidden 7168, 8x8 ranks, node-limited top-8:
+    every one of the 65,536 messages (payload, scales, header) against the
+    oracle's pack, with the used slots renumbered densely on both sides."""
     w = I.LL_DECODE
-    say("LL dispatch full decode shape (sampled rows)")
-    rng = np.random.default_rng(123)
-    sample = np.sort(rng.choice(w.num_tokens, size=96, replace=False))
+    say("LL dispatch full decode shape (all messages)")
     x = I.tokens_for(w)
     scores = I.scores_for(w)
     g = group_for(w)
@@ -291,12 +292,12 @@ def test_ll_dispatch_full_decode_shape():
         np.testing.assert_array_equal(slot, want_slot)
         buf = buffer(g, A.EP_BUF_LL_RECV)
         assert buf.shape == (256 * 64 * 128, 7408)
-        rows = oracle.token_rows(I.bf16_bits(x)[sample], True)
-        for j, i in enumerate(sample):
-            got = host(buf[torch.from_numpy(slot[i].astype(np.int64)).cuda()])
-            np.testing.assert_array_equal(got[:, :7392], np.repeat(rows[j:j + 1], 8, axis=0))
-            np.testing.assert_array_equal(got[:, 7392:].view(np.int32),
-                                          [[i % 128, i // 128, k, 0] for k in range(8)])
+        used = np.unique(slot[slot >= 0])
+        assert len(used) == w.num_tokens * 8
+        dense = np.searchsorted(used, slot).astype(np.int32)     # slot -> its rank among the used slots
+        want = oracle.pack_ll(I.bf16_bits(x), 128, 8, True, dense, len(used))
+        got = host(buf[torch.from_numpy(used.astype(np.int64)).cuda()])
+        np.testing.assert_array_equal(got, want)
         ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
@@ -340,7 +341,15 @@ def _ht_dispatch(w, x, scores, weights, sample=None, in_fp8=False):
             np.testing.assert_array_equal(host(buffer(g, which)[:rows2]), meta[name], err_msg=name)
         st1 = buffer(g, A.EP_BUF_HT_STAGE1)
         st2 = buffer(g, A.EP_BUF_HT_STAGE2)
-        toks = np.arange(S * T) if sample is None else sample
+        if sample is None:
+            # every row of both stages against the oracle's own pack
+            pk = oracle.pack_ht(I.bf16_bits(x), topk, weights, T, w.num_nodes, fp8,
+                                lay["node_row"], lay["row2"], rows1, rows2)
+            np.testing.assert_array_equal(host(st1[:rows1]), pk["stage1"], err_msg="stage 1")
+            np.testing.assert_array_equal(host(st2[:rows2]), pk["stage2"], err_msg="stage 2")
+            ep.ep_destroy_handle(h)
+            return g, topk, lay
+        toks = sample
         img = oracle.token_rows(I.bf16_bits(x)[toks], fp8)
         for j, i in enumerate(toks):
             r1 = node_row[i][node_row[i] >= 0]
@@ -379,14 +388,11 @@ def test_bf16_dispatch_full_hidden():
     chunks, the last one ragged; HT rows and LL messages (header, zero tail)
     equal the oracle's."""
     w = I.HT_PREFILL.with_(tokens_per_rank=300, payload="bf16", seed=43)
-    say("HT dispatch BF16 hidden 7168 (sampled rows)")
-    rng = np.random.default_rng(44)
-    sample = np.sort(rng.choice(300, size=48, replace=False))
-    g, _, _ = _ht_dispatch(w, I.tokens_for(w), I.scores_for(w), I.normal_weights(300, 8, 43), sample=sample)
+    say("HT dispatch BF16 hidden 7168 (all rows)")
+    g, _, _ = _ht_dispatch(w, I.tokens_for(w), I.scores_for(w), I.normal_weights(300, 8, 43))
     ep.ep_destroy_group(g)
-    say("LL dispatch BF16 hidden 7168 (sampled tokens)")
-    _ll_dispatch(2, 64, 256, 8, 7168, "bf16", 64, seed=45, N=8, G=8, M=4,
-                 sample=np.sort(rng.choice(128, size=24, replace=False)))
+    say("LL dispatch BF16 hidden 7168 (all tokens)")
+    _ll_dispatch(2, 64, 256, 8, 7168, "bf16", 64, seed=45, N=8, G=8, M=4)
 
 
 def test_ht_dispatch_prequantised_input():
@@ -398,13 +404,12 @@ def test_ht_dispatch_prequantised_input():
 
 
 def test_ht_dispatch_full_prefill_shape():
-    """The page's shape: 4096 tokens, hidden 7168, seed 0 scores (sampled rows)."""
+    """The page's shape: 4096 tokens, hidden 7168, seed 0 scores: all 16,248
+    stage-1 and 32,768 stage-2 rows and their metadata."""
     w = I.HT_PREFILL
-    say("HT dispatch full prefill shape (sampled rows)")
-    rng = np.random.default_rng(7)
-    sample = np.sort(rng.choice(w.num_tokens, size=128, replace=False))
+    say("HT dispatch full prefill shape (all rows)")
     x = I.tokens_for(w)
-    g, topk, lay = _ht_dispatch(w, x, I.scores_for(w), I.normal_weights(4096, 8, w.seed), sample=sample)
+    g, topk, lay = _ht_dispatch(w, x, I.scores_for(w), I.normal_weights(4096, 8, w.seed))
     try:
         assert lay["c1"].sum() == 16248 and lay["c2"].sum() == 32768
     finally:
@@ -415,11 +420,12 @@ def test_ht_dispatch_full_prefill_shape():
 # A7 combine
 # ---------------------------------------------------------------------------
 
-def test_combine_cfg_geometry_sampled():
+def test_combine_cfg_geometry_all_tokens():
     """4096 tokens x top-8 over 32768 bf16 rows of hidden 7168 (the combine
-    workload); rows placed by the HT handle of the page's routing."""
+    workload); rows placed by the HT handle of the page's routing; every
+    output element against the oracle."""
     w = I.COMBINE
-    say("combine 4096x8x7168 (sampled tokens)")
+    say("combine 4096x8x7168 (all tokens)")
     scores = I.scores_for(w)
     g = group_for(w)
     try:
@@ -431,11 +437,8 @@ def test_combine_cfg_geometry_sampled():
         out = torch.empty((4096, 7168), dtype=torch.bfloat16, device="cuda")
         ep.ep_combine(h, Yt.cuda(), dev(wts), out)
         row2 = get_map(h, A.EP_MAP_HT_ROW)
-        rng = np.random.default_rng(11)
-        which = np.sort(rng.choice(4096, size=48, replace=False))
-        want = oracle.combine(I.bf16_bits(Yt), wts, row2, which=which)
-        got = host(out)[which]
-        np.testing.assert_array_equal(got, want)
+        want = oracle.combine(I.bf16_bits(Yt), wts, row2)
+        np.testing.assert_array_equal(host(out), want)
         assert ep.ep_get_device_error(g) == 0
         ep.ep_destroy_handle(h)
     finally:
@@ -532,15 +535,15 @@ def test_tiny_identity_roundtrip_returns_input(mode):
         ep.ep_destroy_group(g)
 
 
-def test_fp8_roundtrip_large_skewed_sampled():
+def test_fp8_roundtrip_large_skewed_all():
     """16384 tokens, Zipf(1.1) popularity, FP8 dispatch (HT), identity expert,
-    BF16 combine: sampled tokens equal the oracle's round trip bit for bit and
-    stay within the FP8 error bound of the input."""
+    BF16 combine: routing, maps, every stage-1 and stage-2 row, the identity
+    expert's output and every output token equal the oracle's round trip bit
+    for bit, and every token stays within the FP8 error bound of its input."""
     w = I.ROUND_TRIP
-    say("FP8 round trip 16384 tokens (sampled)")
+    say("FP8 round trip 16384 tokens (all rows and tokens)")
     scores = I.scores_for(w)
     x = I.tokens_for(w)
-    wts_all = None
     g = group_for(w)
     try:
         topk_d = torch.empty((w.num_tokens, 8), dtype=torch.int32, device="cuda")
@@ -552,30 +555,33 @@ def test_fp8_roundtrip_large_skewed_sampled():
         ep.ep_dispatch(h, x.cuda(), topk_weights=dev(wts_all))
         n_rows = ep.ep_handle_get_num_recv(h, -1)
         assert n_rows == w.num_tokens * 8
+        lay = oracle.layout_ht(topk, 1, 256, 8, 8)
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_NODE_ROW), lay["node_row"])
+        np.testing.assert_array_equal(row2, lay["row2"])
+        rows1 = int(lay["c1"].sum())
+        pk = oracle.pack_ht(I.bf16_bits(x), topk, wts_all, w.num_tokens, 8, True, lay["node_row"],
+                            lay["row2"], rows1, n_rows)
+        np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE1)[:rows1]), pk["stage1"])
         st2 = buffer(g, A.EP_BUF_HT_STAGE2)[:n_rows]
+        np.testing.assert_array_equal(host(st2), pk["stage2"])
+        y_or = oracle.dequant_rows(pk["stage2"], 7168, True)
+        del pk
         y = torch.empty((n_rows, 7168), dtype=torch.bfloat16, device="cuda")
         ep.ep_dequantize_rows(g, st2, y)
+        np.testing.assert_array_equal(host(y), y_or)
         out = torch.empty((w.num_tokens, 7168), dtype=torch.bfloat16, device="cuda")
         ep.ep_combine(h, y, dev(wts_all), out)
-        row2 = get_map(h, A.EP_MAP_HT_ROW)
-        rng = np.random.default_rng(5)
-        which = np.sort(rng.choice(w.num_tokens, size=40, replace=False))
-        rows_needed = np.unique(row2[which].ravel())
-        st2_rows = host(st2[torch.from_numpy(rows_needed.astype(np.int64)).cuda()])
-        y_or = oracle.dequant_rows(st2_rows, 7168, True)
-        # the oracle's own stage-2 rows of those tokens must equal the GPU's
-        img = oracle.token_rows(I.bf16_bits(x)[which], True)
-        pos = {r: j for j, r in enumerate(rows_needed)}
-        for j, i in enumerate(which):
-            for k in range(8):
-                np.testing.assert_array_equal(st2_rows[pos[row2[i, k]]], img[j])
-        remap = np.vectorize(pos.get)(row2[which]).astype(np.int32)
-        want = oracle.combine(y_or, wts_all[which], remap)
-        got = host(out)[which]
+        del y
+        want = oracle.combine(y_or, wts_all, row2)
+        del y_or
+        got = host(out)
         np.testing.assert_array_equal(got, want)
-        xf = x[which].float().numpy()
+        assert ep.ep_get_device_error(g) == 0
+        # the round trip returns each token within the FP8 error bound
+        xf = x.float().numpy()
         gf = torch.from_numpy(got.view(np.int16)).view(torch.bfloat16).float().numpy()
-        amax = np.abs(xf).reshape(len(which), -1, 128).max(axis=2).repeat(128, axis=1)
+        amax = np.abs(xf).reshape(w.num_tokens, -1, 128).max(axis=2).repeat(128, axis=1)
         assert np.all(np.abs(gf - xf) <= 2.0**-4 * np.abs(xf) + 2.0**-8 * np.abs(xf) + amax * 2.0**-9 + 1e-6)
         ep.ep_destroy_handle(h)
     finally:
