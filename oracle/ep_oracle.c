@@ -61,18 +61,31 @@ float orc_bf16_to_f32(uint16_t b)
 /* float -> bfloat16, round to nearest, ties to even, by definition: the two
  * bf16 neighbours of f are its truncation and the next value away from zero;
  * pick the nearer, and on an exact tie the one whose last mantissa bit is 0.
- * Inputs are finite (NaN is outside the contract). */
+ * Magnitudes from the largest finite bf16 plus half its spacing upwards
+ * round to infinity (IEEE 754 overflow); infinities stay infinite.  NaN is
+ * outside the contract and gives the canonical quiet NaN 0x7FC0. */
 uint16_t orc_f32_to_bf16(float f)
 {
     uint32_t u;
     memcpy(&u, &f, 4);
+    if (f != f) return 0x7FC0;              /* NaN: the canonical quiet NaN */
     uint32_t lo = u & 0xFFFF0000u;          /* truncation toward zero      */
     uint32_t hi = lo + 0x10000u;            /* next bf16 away from zero    */
     if (lo == u) return (uint16_t)(lo >> 16);
-    float flo, fhi;
+    float flo;
     memcpy(&flo, &lo, 4);
-    memcpy(&fhi, &hi, 4);
-    double a = fabs((double)f), dlo = a - fabs((double)flo), dhi = fabs((double)fhi) - a;
+    /* Rounding works as if the exponent range were unbounded: above the
+     * largest finite bf16 the next candidate is 2^128, and choosing it is an
+     * overflow to infinity (hi is then the bit pattern of +-inf). */
+    double hi_mag;
+    if ((hi & 0x7F800000u) == 0x7F800000u) {
+        hi_mag = ldexp(1.0, 128);
+    } else {
+        float fhi;
+        memcpy(&fhi, &hi, 4);
+        hi_mag = fabs((double)fhi);
+    }
+    double a = fabs((double)f), dlo = a - fabs((double)flo), dhi = hi_mag - a;
     if (dlo < dhi) return (uint16_t)(lo >> 16);
     if (dhi < dlo) return (uint16_t)(hi >> 16);
     return (uint16_t)(((lo >> 16) & 1u) ? (hi >> 16) : (lo >> 16));

@@ -26,8 +26,23 @@ def test_bf16_rounding_matches_torch():
     rng = np.random.default_rng(3)
     bits = rng.integers(0, 2**32, size=2_000_000, dtype=np.uint64).astype(np.uint32)
     x = bits.view(np.float32)
-    x = x[np.isfinite(x) & (np.abs(x) < 3.3e38)]
+    x = x[np.isfinite(x)]
     np.testing.assert_array_equal(oracle.f32_to_bf16_array(x), _torch_bf16_bits(x))
+
+
+def test_bf16_rounding_at_overflow_matches_torch():
+    """Every fp32 of the top binade of either sign, and the infinities: from
+    the largest finite bf16 plus half its spacing (0x7F7F8000) upwards the
+    value rounds to infinity, below it to the largest finite bf16."""
+    top = np.arange(0x7F000000, 0x7F800000 + 1, dtype=np.uint64).astype(np.uint32)
+    top = np.concatenate([top, top | np.uint32(0x80000000)])
+    x = top.view(np.float32)
+    got = oracle.f32_to_bf16_array(x)
+    np.testing.assert_array_equal(got, _torch_bf16_bits(x))
+    f = lambda b: oracle.f32_to_bf16(np.array([b], np.uint32).view(np.float32)[0])
+    assert f(0x7F7F7FFF) == 0x7F7F and f(0x7F7F8000) == 0x7F80 and f(0x7F7FFFFF) == 0x7F80
+    assert f(0xFF7F8000) == 0xFF80 and f(0x7F800000) == 0x7F80
+    assert oracle.f32_to_bf16(float("nan")) == 0x7FC0
 
 
 def test_bf16_ties_to_even():
