@@ -457,6 +457,51 @@ def test_combine_all_tokens(n, K, H):
         ep.ep_destroy_group(g)
 
 
+def test_combine_special_values():
+    """Signed zeros, bf16 subnormals (fp32 denormals inside the fma chain: no
+    flush to zero on either side), the smallest and largest normals, bf16
+    rounding ties and sums that overflow to +inf, against the oracle bit for
+    bit.  Large values are positive and weights non-negative, so no inf - inf
+    (NaN inputs and results are outside the contract)."""
+    n, K, H = 256, 8, 256
+    say("combine special values")
+    rng = np.random.default_rng(97)
+    palette = np.array([0x0000, 0x8000, 0x0001, 0x8001, 0x007F, 0x807F, 0x0080, 0x8080,   # zeros, subnormals,
+                        0x7F7F, 0x7F7E, 0x3F80, 0xBF80, 0x3F81, 0xBF81, 0x4000, 0x3F00],   # min normals, max,
+                       np.uint16)                                                         # ±1, ±(1 + ulp), 2, 0.5
+    Y = palette[rng.integers(0, len(palette), size=(n * K, H))]
+    Y[::5] = I.bf16_bits(I.normal_bf16(len(Y[::5]), H, 98))                  # ordinary rows mixed in
+    wpal = np.array([0.0, -0.0, 1.0, 0.5, 2.0, 1e-39, 1.5e-45, 0.75, 1.0 + 2.0**-23], np.float32)
+    wts = wpal[rng.integers(0, len(wpal), size=(n, K))]
+    wts[:, 0] = np.where(rng.random(n) < 0.5, wts[:, 0], 1.0)
+    wts[rng.random((n, K)) < 0.02] = 3.0e38      # a few huge weights: overflow to +inf
+    # no negative huge products: a huge weight only meets rows without negative values
+    topk = I.random_topk(n, 4 * K, K, seed=99)
+    g = ep.ep_create_group(mode="ht", num_nodes=1, ranks_per_node=1, num_experts=4 * K, top_k=K,
+                           max_nodes_per_token=0, hidden=H, max_tokens_per_rank=n,
+                           num_src_ranks=1, payload="bf16")
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        row2 = get_map(h, A.EP_MAP_HT_ROW)
+        big = wts > 2.0
+        for t, k in zip(*np.nonzero(big)):
+            r = Y[row2[t, k]]
+            neg = (r & 0x8000) != 0
+            r[neg] = 0x8000                      # -0 instead of a negative value
+            Y[row2[t, k]] = r
+        want = oracle.combine(Y, wts, row2)
+        wf = torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy()
+        assert not np.isnan(wf).any()
+        assert np.isposinf(wf).any() and (want == 0x8000).any() and ((want & 0x7F80) == 0).any()
+        Yt = torch.from_numpy(Y.view(np.int16)).view(torch.bfloat16).cuda()
+        out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(h, Yt, dev(wts), out)
+        np.testing.assert_array_equal(host(out), want)
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
 def test_combine_invalid_and_out_of_range_rows():
     n, K, H = 40, 4, 256
     topk = I.random_topk(n, 16, K, seed=3)
