@@ -58,3 +58,16 @@ def test_stored_traffic_is_consistent():
         t = bench.stored_traffic(kernel)
         if t is not None:       # only while the kernel sources match the profiled ones
             assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
+
+
+def test_cpu_baseline_object(monkeypatch):
+    """The oracle leg: one whole run of the 4096-token step on the host,
+    reported as the oracle with the threads it used and what it ran."""
+    import ep_inputs as I
+    monkeypatch.setattr(bench, "MIN_CPU_SECONDS", 0.0)
+    w = I.HT_PREFILL
+    cb = bench.cpu_baseline(I.scores_for(w), I.tokens_for(w), I.normal_weights(4096, 8, w.seed),
+                            I.normal_bf16(4096 * 8, 7168, I.COMBINE.seed), 4096)
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1 and cb["runs"] == 1
+    assert cb["value"] > 0 and "4096 tokens" in cb["sample"]
+    assert abs(cb["value"] - 955_810_496 / cb["seconds"] / 1e9) <= 0.01 * cb["value"]
