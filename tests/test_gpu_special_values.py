@@ -110,3 +110,43 @@ def test_backward_special_values():
         ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+def _node_scores_ok(s, N, J):
+    """True when no node score (float32 sum of the node's J largest scores,
+    largest first) is NaN, i.e. no +inf meets -inf."""
+    P = s.shape[1] // N
+    top = -np.sort(-s.reshape(len(s), N, P), axis=2)[:, :, :J]
+    with np.errstate(invalid="ignore", over="ignore"):
+        acc = top[:, :, 0].astype(np.float32)
+        for j in range(1, J):
+            acc = (acc + top[:, :, j]).astype(np.float32)
+    return ~np.isnan(acc).any(axis=1)
+
+
+@pytest.mark.parametrize("E,N,G,K,M", [(256, 8, 8, 8, 4), (96, 4, 2, 6, 2), (256, 8, 8, 8, 0)])
+def test_route_special_scores(E, N, G, K, M):
+    """Infinities, the largest finite floats (node scores that overflow to
+    +inf and tie), subnormals, signed zeros and negatives, on the fast and
+    the generic routing kernels."""
+    n = 512
+    say(f"route special scores E={E} M={M}")
+    pal = np.array([np.inf, 3.4028235e38, 3.0e38, 1.0e38, 1.0, 1e-40, -1e-40, 1.4e-45, 0.0, -0.0,
+                    -1.0, -3.0e38, -np.inf], np.float32)
+    rng = np.random.default_rng(E + K + M)
+    s = pal[rng.integers(0, len(pal), size=(n, E))]
+    s[::3] = np.where(rng.random((len(s[::3]), E)) < 0.5, 1e-40, -0.0).astype(np.float32)
+    J = (K + M - 1) // M if 0 < M < N else 1
+    if 0 < M < N:
+        bad = ~_node_scores_ok(s, N, J)
+        s[bad] = np.abs(s[bad])                  # no -inf left: no inf - inf in a node score
+        assert _node_scores_ok(s, N, J).all()
+    g = ep.ep_create_group(mode="ht", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=128, max_tokens_per_rank=n,
+                           num_src_ranks=1, payload="fp8")
+    try:
+        out = torch.full((n, K), -7, dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(s), out)
+        np.testing.assert_array_equal(host(out), oracle.route(s, N, K, M))
+    finally:
+        ep.ep_destroy_group(g)
