@@ -277,7 +277,11 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  * stage, and recv_counts must stay valid until then.  In LL the group keeps
  * ll_buffers receive buffers and each dispatch takes the next one in turn
  * (ep_handle_get_buffer returns the handle's); with two, a dispatch may be
- * in flight while the previous handle is combined.
+ * in flight while the previous handle is combined.  In HT the group has one
+ * set of stage-1 / stage-2 buffers: each HT dispatch overwrites the rows of
+ * the group's previous one, so a handle's rows and partitions hold its data
+ * until the next dispatch on the group (its maps and counts, and so its
+ * combine, stay valid).
  *   tokens : BF16 [n, H] (n as in the handle), rows 16-byte aligned; or
  *            FP8_E4M3 [n, H] together with
  *   scales : F32 [n, H/128] (tag SCALES) -- already quantised tokens are
