@@ -617,3 +617,42 @@ def test_fp8_roundtrip_large_skewed_all():
         ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+def test_ht_two_live_handles():
+    """Two live HT handles on one group: the second dispatch overwrites the
+    group's stage rows with its own, and the first handle keeps its maps, so
+    each handle's combine equals the oracle's for its own routing."""
+    w = I.HT_PREFILL.with_(tokens_per_rank=300, hidden=512, seed=51)
+    say("HT two live handles")
+    g = group_for(w)
+    try:
+        xs, tks, hs, lays = [], [], [], []
+        for j in range(2):
+            scores = I.scores_for(w.with_(seed=51 + j))
+            topk_d = torch.empty((300, 8), dtype=torch.int32, device="cuda")
+            ep.ep_route(g, dev(scores), topk_d)
+            tks.append(host(topk_d))
+            hs.append(ep.ep_create_handle(g, topk_d))
+            lays.append(oracle.layout_ht(tks[j], 1, 256, 8, 8))
+            xs.append(I.normal_bf16(300, 512, 52 + j))
+        assert not np.array_equal(tks[0], tks[1])
+        wts = I.normal_weights(300, 8, 53)
+        for j in range(2):
+            ep.ep_dispatch(hs[j], xs[j].cuda(), topk_weights=dev(wts))
+        # the group's stage-2 rows are the second dispatch's
+        rows2 = int(lays[1]["c2"].sum())
+        pk = oracle.pack_ht(I.bf16_bits(xs[1]), tks[1], wts, 300, 8, True, lays[1]["node_row"],
+                            lays[1]["row2"], int(lays[1]["c1"].sum()), rows2)
+        np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2)[:rows2]), pk["stage2"])
+        for j in (0, 1):
+            np.testing.assert_array_equal(get_map(hs[j], A.EP_MAP_HT_ROW), lays[j]["row2"])
+            Y = I.normal_bf16(300 * 8, 512, 54 + j)
+            out = torch.empty((300, 512), dtype=torch.bfloat16, device="cuda")
+            ep.ep_combine(hs[j], Y.cuda(), dev(wts), out)
+            np.testing.assert_array_equal(host(out), oracle.combine(I.bf16_bits(Y), wts, lays[j]["row2"]))
+        assert ep.ep_get_device_error(g) == 0
+        for h in hs:
+            ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
