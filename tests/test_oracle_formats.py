@@ -229,3 +229,41 @@ def test_combine_within_fp64_error_bound():
     mag = np.einsum("nk,nkh->nh", np.abs(w.astype(np.float64)), np.abs(Yf[loc]))
     bound = K * 2.0**-24 * mag + 2.0**-8 * np.abs(exact) + 1e-40
     assert np.all(np.abs(out - exact) <= bound)
+
+
+def _bf16_exact(values):
+    """bf16 bit patterns of values bf16 holds exactly."""
+    u = np.array(values, np.float32).view(np.uint32)
+    assert np.all((u & 0xFFFF) == 0)
+    return (u >> 16).astype(np.uint16)
+
+
+def test_combine_is_a_fused_multiply_add_chain():
+    """Worked by hand.  Weights -(1+2^-23) and 1+2^-23 on two rows of
+    1+2^-7: the first step rounds -(1+2^-7+2^-23+2^-30) to -(1+2^-7+2^-23);
+    a fused second step then leaves exactly 2^-30 (bf16 0x3080), whereas a
+    product rounded before the add would cancel to 0."""
+    Y = np.tile(_bf16_exact([1 + 2.0**-7]), (2, 4))
+    w = np.array([[-(1 + 2.0**-23), 1 + 2.0**-23]], np.float32)
+    out = oracle.combine(Y, w, np.array([[0, 1]], np.int32))
+    assert np.all(out == 0x3080) and _bf16_exact([2.0**-30])[0] == 0x3080
+
+
+def test_combine_accumulates_in_k_order():
+    """Worked by hand.  Rows 2^24, 1, -2^24 with unit weights: in k order
+    2^24 + 1 is a tie that rounds to 2^24 (even) and the sum ends at +0; in
+    the reverse order -2^24 + 1 is exact and the sum ends at 1."""
+    rows = _bf16_exact([2.0**24, 1.0, -2.0**24])
+    Y = np.repeat(rows[:, None], 4, axis=1)
+    w = np.ones((2, 3), np.float32)
+    out = oracle.combine(Y, w, np.array([[0, 1, 2], [2, 1, 0]], np.int32))
+    assert np.all(out[0] == 0x0000) and np.all(out[1] == 0x3F80)
+
+
+def test_combine_starts_from_plus_zero():
+    """Every product is -0 (1 * -0, and -0 * +0): the chain from +0 ends at
+    +0, where starting from -0 or from the first product would give -0."""
+    Y = np.array([[0x8000] * 4, [0x0000] * 4], np.uint16)
+    w = np.array([[1.0, -0.0]], np.float32)
+    out = oracle.combine(Y, w, np.array([[0, 1]], np.int32))
+    assert np.all(out == 0x0000)
