@@ -37,11 +37,16 @@ _lib = None
 
 
 def lib() -> ctypes.CDLL:
+    """The oracle library; EP_ORACLE_LIB names another build of ep_oracle.c
+    (the pin tests' mutation check loads deliberately broken copies)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build()
-        _lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("EP_ORACLE_LIB")
+        if not path:
+            path = _LIB
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build()
+        _lib = ctypes.CDLL(path)
         _declare(_lib)
     return _lib
 

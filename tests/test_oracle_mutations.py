@@ -1,0 +1,105 @@
+"""The pins have teeth: copies of ep_oracle.c with one plausible mistake
+each -- a wrong tie rule, a dropped term, a wrong index, order or starting
+value -- are built, and the pins that cover that step must fail on every one.
+
+Each mutant runs the named pin tests in a child pytest process with
+EP_ORACLE_LIB pointing at the mutant's library; exit status 1 means that
+tests ran and failed.  The unmutated source, built the same way, passes
+them all (the control).
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ep_oracle.c")
+F = "tests/test_oracle_formats.py::"
+R = "tests/test_oracle_route.py::"
+L = "tests/test_oracle_layout.py::"
+
+# (name, text in ep_oracle.c, replacement (every occurrence), pins that must fail)
+MUTANTS = [
+    ("bf16 ties round away from zero",
+     "return (uint16_t)(((lo >> 16) & 1u) ? (hi >> 16) : (lo >> 16));",
+     "return (uint16_t)(hi >> 16);",
+     [F + "test_bf16_ties_to_even"]),
+    ("bf16 saturates instead of overflowing",
+     "hi_mag = ldexp(1.0, 128);", "hi_mag = INFINITY;",
+     [F + "test_bf16_rounding_at_overflow_matches_torch"]),
+    ("E4M3 ties go to the lower code",
+     "else code = (lo & 1) ? hi : lo;", "else code = lo;",
+     [F + "test_e4m3_encode_boundaries_match_torch"]),
+    ("E4M3 saturates at 240 (the FNUZ maximum)",
+     "if (a >= 448.0) return sign | 0x7E;", "if (a >= 240.0) return sign | 0x77;",
+     [F + "test_e4m3_encode_strided_sweep_matches_torch"]),
+    ("quotient through the reciprocal scale",
+     "float v = orc_bf16_to_f32(x[b * 128 + j]) / scale;",
+     "float v = orc_bf16_to_f32(x[b * 128 + j]) * (448.0f / amax);",
+     [F + "test_quantize_matches_torch_blockwise"]),
+    ("node score drops its second term",
+     "for (int j = 0; j < J; ++j) {", "for (int j = 0; j < (J > 1 ? J - 1 : 1); ++j) {",
+     [R + "test_c_oracle_matches_page_study"]),
+    ("expert ties go to the higher index",
+     "if (allowed[e] && !taken[e] && (best < 0 || s[e] > s[best])) best = e;",
+     "if (allowed[e] && !taken[e] && (best < 0 || s[e] >= s[best])) best = e;",
+     [R + "test_forced_ties_follow_lower_index"]),
+    ("LL slots counted across sources",
+     "const int slot = counts[e * S + s]++;", "const int slot = counts[e * S]++;",
+     [L + "test_ll_brute_force_tiny"]),
+    ("same-position rank from s / G",
+     "n * G + s % G", "n * G + s / G",
+     [L + "test_ht_brute_force_tiny"]),
+    ("combine rounds the product before the add",
+     "acc = fmaf(w[i * K + k], orc_bf16_to_f32(Y[(int64_t)r * ld_y + h]), acc);",
+     "acc = acc + w[i * K + k] * orc_bf16_to_f32(Y[(int64_t)r * ld_y + h]);",
+     [F + "test_combine_is_a_fused_multiply_add_chain"]),
+    ("combine in reverse k order",
+     "            for (int k = 0; k < K; ++k) {\n                const int32_t r = loc[i * K + k];\n"
+     "                if (r < 0) continue;\n                acc = fmaf(",
+     "            for (int k = K - 1; k >= 0; --k) {\n                const int32_t r = loc[i * K + k];\n"
+     "                if (r < 0) continue;\n                acc = fmaf(",
+     [F + "test_combine_accumulates_in_k_order"]),
+    ("combine starts from -0",
+     "            float acc = 0.0f;\n            for (int k = 0; k < K; ++k) {\n"
+     "                const int32_t r = loc[i * K + k];\n                if (r < 0) continue;\n"
+     "                acc = fmaf(",
+     "            float acc = -0.0f;\n            for (int k = 0; k < K; ++k) {\n"
+     "                const int32_t r = loc[i * K + k];\n                if (r < 0) continue;\n"
+     "                acc = fmaf(",
+     [F + "test_combine_starts_from_plus_zero"]),
+    ("identity expert reads the wrong block's scale",
+     "memcpy(&sc, src + H + 4 * (h / 128), 4);", "memcpy(&sc, src + H + 4 * ((h / 128) ^ 1), 4);",
+     [F + "test_dequant_matches_torch"]),
+]
+
+
+def _build(tmp_path, name, text):
+    c = tmp_path / f"{name}.c"
+    c.write_text(text)
+    so = tmp_path / f"{name}.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC", str(c), "-o", str(so),
+                    "-lm"], check=True, capture_output=True)
+    return str(so)
+
+
+def _run_pins(lib, pins):
+    env = dict(os.environ, EP_ORACLE_LIB=lib)
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", *pins],
+                          cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+
+
+def test_control_passes(tmp_path):
+    lib = _build(tmp_path, "control", open(SRC).read())
+    r = _run_pins(lib, sorted({p for m in MUTANTS for p in m[3]}))
+    assert r.returncode == 0, r.stdout[-3000:]
+
+
+@pytest.mark.parametrize("name,old,new,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new, pins):
+    src = open(SRC).read()
+    assert old in src, "the mutated text must exist in the oracle"
+    lib = _build(tmp_path, "mutant", src.replace(old, new))
+    r = _run_pins(lib, pins)
+    assert r.returncode == 1, f"pins {pins} did not catch: {name}\n{r.stdout[-2000:]}"
