@@ -205,3 +205,41 @@ def test_pack_roundtrip_headers():
             m = buf[slot_map[i, k]]
             np.testing.assert_array_equal(m[:rb], rows[i])
             assert list(m[rb:].view(np.int32)) == [i % T, i // T, k, 0]
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_ht_pack_rows_and_metadata_roundtrip(S):
+    """Every HT row holds the image of the token its map entry names, and its
+    metadata names that entry back: stage 1 (token, source, the token's
+    top-k and weights) at node_row(i, n); stage 2 (source, token, k) at
+    row2(i, k).  Rows no entry names do not exist (the counts are exact)."""
+    T, K, E, N, G, H = 40, 4, 32, 4, 2, 256
+    topk = I.random_topk(S * T, E, K, seed=60 + S)
+    topk[5, 1] = topk[5, 0]                       # a repeated entry: no row
+    w = np.random.default_rng(61).random((S * T, K)).astype(np.float32)
+    x = I.bf16_bits(I.normal_bf16(S * T, H, seed=62))
+    lay = oracle.layout_ht(topk, S, E, N, G)
+    rows1, rows2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+    pk = oracle.pack_ht(x, topk, w, T, N, True, lay["node_row"], lay["row2"], rows1, rows2)
+    img = oracle.token_rows(x, True)
+    seen1, seen2 = set(), set()
+    for i in range(S * T):
+        s, t = divmod(i, T)
+        for n in range(N):
+            r = lay["node_row"][i, n]
+            if r < 0:
+                continue
+            seen1.add(int(r))
+            np.testing.assert_array_equal(pk["stage1"][r], img[i])
+            assert pk["meta1_tok"][r] == t and pk["meta1_src"][r] == s
+            np.testing.assert_array_equal(pk["meta1_topk"][r], topk[i])
+            np.testing.assert_array_equal(pk["meta1_w"][r], w[i])
+        for k in range(K):
+            r = lay["row2"][i, k]
+            if r < 0:
+                continue
+            seen2.add(int(r))
+            np.testing.assert_array_equal(pk["stage2"][r], img[i])
+            assert (pk["meta2_src"][r], pk["meta2_tok"][r], pk["meta2_k"][r]) == (s, t, k)
+    assert seen1 == set(range(rows1)) and seen2 == set(range(rows2))
+    assert lay["row2"][5, 1] == -1
