@@ -69,6 +69,39 @@ MUTANTS = [
      "                const int32_t r = loc[i * K + k];\n                if (r < 0) continue;\n"
      "                acc = fmaf(",
      [F + "test_combine_starts_from_plus_zero"]),
+    ("node ties go to the higher index",
+     "node_score[n] > node_score[best]", "node_score[n] >= node_score[best]",
+     [R + "test_forced_ties_follow_lower_index"]),
+    ("amax misses a block's last element",
+     "for (int j = 0; j < 128; ++j) {\n            float a = fabsf",
+     "for (int j = 0; j < 127; ++j) {\n            float a = fabsf",
+     [F + "test_quantize_matches_torch_blockwise"]),
+    ("the inverse scale is stored",
+     "scales[b] = scale;", "scales[b] = 1.0f / scale;",
+     [F + "test_quantize_matches_torch_blockwise"]),
+    ("LL header fields swapped",
+     "int32_t hdr[4] = {(int32_t)(i % T), (int32_t)(i / T), k, 0};",
+     "int32_t hdr[4] = {(int32_t)(i / T), (int32_t)(i % T), k, 0};",
+     [L + "test_pack_roundtrip_headers"]),
+    ("stage-1 metadata names the global token index",
+     "meta1_tok[r] = t;", "meta1_tok[r] = (int32_t)i;",
+     [L + "test_ht_pack_rows_and_metadata_roundtrip"]),
+    ("stage-1 weights not forwarded",
+     "if (w) meta1_w[(int64_t)r * K + k] = w[i * K + k];", "if (w) meta1_w[(int64_t)r * K + k] = 0.0f;",
+     [L + "test_ht_pack_rows_and_metadata_roundtrip"]),
+    ("stage-2 metadata source and token swapped",
+     "meta2_src[r] = s;\n            meta2_tok[r] = t;", "meta2_src[r] = t;\n            meta2_tok[r] = s;",
+     [L + "test_ht_pack_rows_and_metadata_roundtrip"]),
+    ("stage-2 k off by one",
+     "meta2_k[r] = k;", "meta2_k[r] = k + 1;",
+     [L + "test_ht_pack_rows_and_metadata_roundtrip"]),
+    ("row gradient drops the weight",
+     "const float prod = w[t * K + k] * gv;", "const float prod = gv;",
+     ["tests/test_oracle_backward.py::test_row_gradient_rounding_matches_torch"]),
+    ("weight gradient drops a term",
+     "for (int h = 0; h < H; ++h) {\n                    const float gv",
+     "for (int h = 0; h < H - 1; ++h) {\n                    const float gv",
+     ["tests/test_oracle_backward.py::test_weight_gradient_is_the_derivative"]),
     ("identity expert reads the wrong block's scale",
      "memcpy(&sc, src + H + 4 * (h / 128), 4);", "memcpy(&sc, src + H + 4 * ((h / 128) ^ 1), 4);",
      [F + "test_dequant_matches_torch"]),
@@ -86,7 +119,7 @@ def _build(tmp_path, name, text):
 
 def _run_pins(lib, pins):
     env = dict(os.environ, EP_ORACLE_LIB=lib)
-    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-p", "no:cacheprovider", *pins],
+    return subprocess.run([sys.executable, "-m", "pytest", "-q", "-x", "-p", "no:cacheprovider", *pins],
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
