@@ -7,6 +7,7 @@ EP_ORACLE_LIB pointing at the mutant's library; exit status 1 means that
 tests ran and failed.  The unmutated source, built the same way, passes
 them all (the control).
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -108,13 +109,14 @@ MUTANTS = [
 ]
 
 
-def _build(tmp_path, name, text):
-    c = tmp_path / f"{name}.c"
-    c.write_text(text)
-    so = tmp_path / f"{name}.so"
-    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC", str(c), "-o", str(so),
-                    "-lm"], check=True, capture_output=True)
-    return str(so)
+def _build(d, name, text):
+    c = os.path.join(d, f"{name}.c")
+    with open(c, "w") as f:
+        f.write(text)
+    so = os.path.join(d, f"{name}.so")
+    subprocess.run(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-shared", "-fPIC", c, "-o", so, "-lm"],
+                   check=True, capture_output=True)
+    return so
 
 
 def _run_pins(lib, pins):
@@ -123,16 +125,32 @@ def _run_pins(lib, pins):
                           cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
 
 
-def test_control_passes(tmp_path):
-    lib = _build(tmp_path, "control", open(SRC).read())
-    r = _run_pins(lib, sorted({p for m in MUTANTS for p in m[3]}))
+@pytest.fixture(scope="module")
+def outcomes(tmp_path_factory):
+    """Every mutant (and the control) built and run, a few at a time."""
+    d = str(tmp_path_factory.mktemp("mutants"))
+    src = open(SRC).read()
+    jobs = {"control": (src, sorted({p for m in MUTANTS for p in m[3]}))}
+    for name, old, new, pins in MUTANTS:
+        jobs[name] = (src.replace(old, new) if old in src else None, pins)
+
+    def run(item):
+        idx, (key, (text, pins)) = item
+        if text is None:
+            return key, None
+        return key, _run_pins(_build(d, f"m{idx}", text), pins)
+
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(6, os.cpu_count() or 1)) as ex:
+        return dict(ex.map(run, enumerate(jobs.items())))
+
+
+def test_control_passes(outcomes):
+    r = outcomes["control"]
     assert r.returncode == 0, r.stdout[-3000:]
 
 
 @pytest.mark.parametrize("name,old,new,pins", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_mutant_is_caught(tmp_path, name, old, new, pins):
-    src = open(SRC).read()
-    assert old in src, "the mutated text must exist in the oracle"
-    lib = _build(tmp_path, "mutant", src.replace(old, new))
-    r = _run_pins(lib, pins)
+def test_mutant_is_caught(outcomes, name, old, new, pins):
+    r = outcomes[name]
+    assert r is not None, "the mutated text must exist in the oracle"
     assert r.returncode == 1, f"pins {pins} did not catch: {name}\n{r.stdout[-2000:]}"
