@@ -80,9 +80,11 @@ def _brute_route(s, nodes, k, m):
     return sorted(best_set, key=lambda e: -float(s[e]))
 
 
-@pytest.mark.parametrize("seed", range(4))
-def test_brute_force_tiny(seed):
-    E, N, K, M = 16, 4, 4, 2
+@pytest.mark.parametrize("seed,E,N,K,M", [(0, 16, 4, 4, 2), (1, 16, 4, 4, 2), (2, 16, 4, 4, 2),
+                                         (3, 16, 4, 4, 2),
+                                         # K not a multiple of M: ceil(K/M) terms per node score
+                                         (4, 16, 4, 3, 2), (5, 24, 4, 5, 3), (6, 20, 5, 7, 3)])
+def test_brute_force_tiny(seed, E, N, K, M):
     s = I.uniform_scores(40, E, seed=100 + seed).astype(np.float32)
     got = oracle.route(s, N, K, M)
     for t in range(s.shape[0]):
