@@ -42,6 +42,16 @@ MUTANTS = [
     ("node score drops its second term",
      "for (int j = 0; j < J; ++j) {", "for (int j = 0; j < (J > 1 ? J - 1 : 1); ++j) {",
      [R + "test_c_oracle_matches_page_study"]),
+    ("node score takes floor(K/M) terms",
+     "const int J = limited ? (K + M - 1) / M : 0;", "const int J = limited ? (K / M > 0 ? K / M : 1) : 0;",
+     [R + "test_brute_force_tiny"]),
+    ("one node fewer is kept",
+     "for (int m = 0; m < M; ++m) {", "for (int m = 0; m < M - 1; ++m) {",
+     [R + "test_brute_force_tiny"]),
+    ("repeated entries get a slot",
+     "if (row[j] == e) { *err |= ORC_ERR_DUP_INDEX; return 0; }",
+     "if (row[j] == e) { *err |= ORC_ERR_DUP_INDEX; return 1; }",
+     [L + "test_ll_brute_force_tiny"]),
     ("expert ties go to the higher index",
      "if (allowed[e] && !taken[e] && (best < 0 || s[e] > s[best])) best = e;",
      "if (allowed[e] && !taken[e] && (best < 0 || s[e] >= s[best])) best = e;",
