@@ -113,6 +113,27 @@ MUTANTS = [
      "for (int h = 0; h < H; ++h) {\n                    const float gv",
      "for (int h = 0; h < H - 1; ++h) {\n                    const float gv",
      ["tests/test_oracle_backward.py::test_weight_gradient_is_the_derivative"]),
+    ("E4M3 drops the sign of zero",
+     "uint8_t sign = signbit(v) ? 0x80 : 0x00;", "uint8_t sign = (v < 0) ? 0x80 : 0x00;",
+     [F + "test_e4m3_signed_zero_and_saturation"]),
+    ("an all-zero block gets codes 0x80",
+     "            memset(q + b * 128, 0, 128);", "            memset(q + b * 128, 0x80, 128);",
+     [F + "test_quantize_matches_torch_blockwise"]),
+    ("a row's scales in reverse block order",
+     "memcpy(dst + H, sc, sizeof(float) * (size_t)(H / 128));",
+     "for (int b_ = 0; b_ < H / 128; ++b_) memcpy(dst + H + 4 * b_, &sc[H / 128 - 1 - b_], 4);",
+     [F + "test_row_image_layout"]),
+    ("combine reads row 0 for an invalid entry",
+     "                if (r < 0) continue;\n                acc = fmaf(",
+     "                const int32_t rr = r < 0 ? 0 : r;\n"
+     "                acc = fmaf(w[i * K + k], orc_bf16_to_f32(Y[(int64_t)rr * ld_y + h]), acc); continue;\n"
+     "                acc = fmaf(",
+     [F + "test_combine_skips_invalid_and_k1_copy"]),
+    ("a per-rank row belongs to the token's last entry on the rank",
+     "            if (hit[r]) continue;\n            hit[r] = 1;",
+     "            if (hit[r]) { for (int q_ = 0; q_ < k; ++q_) if (row2[i*K+q_] >= 0 && row[q_] / L == r)"
+     " { row2[i*K+k] = row2[i*K+q_]; row2[i*K+q_] = -1; } continue; }\n            hit[r] = 1;",
+     ["tests/test_oracle_rank_dedup.py::test_brute_force_rows"]),
     ("identity expert reads the wrong block's scale",
      "memcpy(&sc, src + H + 4 * (h / 128), 4);", "memcpy(&sc, src + H + 4 * ((h / 128) ^ 1), 4);",
      [F + "test_dequant_matches_torch"]),
