@@ -12,8 +12,8 @@
 //
 // Mapping: a token is split over W waves, each owning a contiguous range of
 // 64*NV chunks (16 elements; 8 with a BF16 payload; lane l: chunks
-// c0 + v*64, v < NV); four waves per 256-thread workgroup and no barriers --
-// each wave ranks its token itself.
+// c0 + v*64, v < NV); the waves of a workgroup (4 in HT, 2 in LL) work on
+// their own with no barriers -- each wave ranks its token itself.
 //  1. The token's payload loads are issued first (16-byte loads).
 //  2. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 (IEEE fp32 division)
@@ -194,7 +194,7 @@ __device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool p
   }
 }
 
-// A token spans W waves, four waves per 256-thread workgroup; a lane owns
+// A token spans W waves, blockDim.x / 64 waves per workgroup; a lane owns
 // chunks c = v*64 + lane, v < NV, of its wave's range (16 elements each; 8
 // with a BF16 payload, a plain 16-byte copy).  No barriers: everything shared
 // inside a token is wave-uniform.
