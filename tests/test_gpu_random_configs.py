@@ -99,3 +99,85 @@ def test_random_config_whole_path(seed):
         ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("seed", range(48))
+def test_random_config_variants(seed):
+    """The same draws with the other features: HT with the per-rank stage 2
+    (unit-weight combine of rank rows), LL staged (send_only + ep_complete for
+    dispatch and combine), and in both modes the backward adjoints on the
+    handle -- row gradients and token gradients bit for bit, weight gradients
+    within the fp32 dot-product bound."""
+    c = _draw(7000 + seed)
+    N, G, E, K, M, S, T, H = c["N"], c["G"], c["E"], c["K"], c["M"], c["S"], c["T"], c["H"]
+    fp8, ll = c["payload"] == "fp8", c["mode"] == "ll"
+    per_rank = (not ll) and seed % 2 == 0
+    R, n = N * G, S * T
+    say(f"random variant {seed}: {c} per_rank={per_rank}")
+    scores = I.uniform_scores(n, E, seed=8000 + seed).astype(np.float32)
+    x = I.normal_bf16(n, H, 9000 + seed)
+    wts = I.normal_weights(n, K, 10000 + seed)
+    T_max = T + int(seed % 2)
+    g = ep.ep_create_group(mode=c["mode"], num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=H, max_tokens_per_rank=T_max, num_src_ranks=S,
+                           payload=c["payload"], ht_stage2="rank" if per_rank else "expert")
+    try:
+        topk_d = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, N, K, M))
+        h = ep.ep_create_handle(g, topk_d)
+        xb = I.bf16_bits(x)
+        if ll:
+            counts = torch.zeros((E, S), dtype=torch.int32, device="cuda")
+            ep.ep_dispatch(h, x.cuda(), recv_counts=counts, send_only=True)
+            ep.ep_complete(h)
+            cnt, loc, _ = oracle.layout_ll(topk, S, E, T_max)
+            np.testing.assert_array_equal(host(counts), cnt)
+            used = np.unique(loc[loc >= 0])
+            dense = np.where(loc >= 0, np.searchsorted(used, loc), -1).astype(np.int32)
+            got = host(ep.ep_handle_get_buffer(h, A.EP_BUF_LL_RECV)[torch.from_numpy(used.astype(np.int64)).cuda()])
+            np.testing.assert_array_equal(got, oracle.pack_ll(xb, T, K, fp8, dense, len(used)))
+            rows = E * S * T_max
+        else:
+            ep.ep_dispatch(h, x.cuda(), topk_weights=dev(wts))
+            lay1 = oracle.layout_ht(topk, S, E, N, G)
+            lay = oracle.layout_ht_rank(topk, S, E, R) if per_rank else lay1
+            loc = lay["row2"]
+            np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_ROW), loc)
+            r1, r2 = int(lay1["c1"].sum()), int(lay["c2"].sum())
+            pk = oracle.pack_ht(xb, topk, wts, T, N, fp8, lay1["node_row"], loc, r1, r2)
+            np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2)[:r2]), pk["stage2"])
+            if per_rank:
+                mt, mw = oracle.meta_ht_rank(topk, wts, loc, E, R, r2)
+                np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2_TOPK)[:r2]), mt)
+                np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2_WEIGHTS)[:r2]), mw)
+            rows = max(r2, 1)
+        Y = I.normal_bf16(rows, H, 11000 + seed)
+        Yd = Y.cuda().view(E, S * T_max, H) if ll else Y.cuda()
+        out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        if ll:
+            ep.ep_combine(h, Yd, dev(wts), out, send_only=True)
+            ep.ep_complete(h)
+        else:
+            ep.ep_combine(h, Yd, None if per_rank else dev(wts), out)
+        cw = np.ones((n, K), np.float32) if per_rank else wts
+        np.testing.assert_array_equal(host(out), oracle.combine(I.bf16_bits(Y), cw, loc))
+        if not per_rank:
+            gb = I.bf16_bits(I.normal_bf16(n, H, 12000 + seed))
+            dY = torch.zeros(Yd.shape, dtype=torch.bfloat16, device="cuda")
+            dw = torch.empty((n, K), dtype=torch.float32, device="cuda")
+            ep.ep_combine_backward(h, torch.from_numpy(gb.view(np.int16)).view(torch.bfloat16).cuda(),
+                                   dev(wts), dY, expert_out=Yd, grad_weights=dw)
+            want_dY, want_dw, absum = oracle.combine_backward(gb, wts, loc, rows, I.bf16_bits(Y))
+            used = np.unique(loc[loc >= 0])
+            np.testing.assert_array_equal(host(dY.view(rows, H))[used], want_dY[used])
+            bound = 2.0 * H * 2.0**-24 * absum + 1e-30
+            assert np.all(np.abs(host(dw).astype(np.float64) - want_dw) <= bound)
+            gx = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+            ep.ep_dispatch_backward(h, Yd, gx)
+            np.testing.assert_array_equal(host(gx), oracle.dispatch_backward(I.bf16_bits(Y), loc))
+        assert ep.ep_get_device_error(g) == 0
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
