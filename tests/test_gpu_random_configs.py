@@ -181,3 +181,65 @@ def test_random_config_variants(seed):
         ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+def _draw_large(seed):
+    rng = np.random.default_rng(seed)
+    N = int(rng.choice([2, 4, 8, 16]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    R = N * G
+    L = int(rng.choice([l for l in (1, 2, 4, 8, 16) if R * l <= 1024]))
+    E = R * L
+    K = int(rng.integers(1, min(E, 16) + 1))
+    P = E // N
+    Ms = [0] + [m for m in range(1, N) if -(-K // m) <= P and m * P >= K]
+    return dict(N=N, G=G, E=E, K=K, M=int(rng.choice(Ms)), S=int(rng.integers(1, min(R, 6) + 1)),
+                T=int(rng.integers(200, 2500)), mode=str(rng.choice(["ll", "ht"])))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_large_batches_layout_and_rows(seed):
+    """Larger random batches (200-2500 tokens per source, up to 6 sources, up
+    to 16 nodes, up to 1024 experts): many tiles per key, so the scans'
+    chunked paths, in registers and in memory, run.
+    Routing, maps, counts and every row or message (FP8, hidden 128) against
+    the oracle."""
+    c = _draw_large(13000 + seed)
+    N, G, E, K, M, S, T = c["N"], c["G"], c["E"], c["K"], c["M"], c["S"], c["T"]
+    ll, H, n = c["mode"] == "ll", 128, S * T
+    say(f"random large batch {seed}: {c}")
+    scores = I.uniform_scores(n, E, seed=14000 + seed).astype(np.float32)
+    x = I.normal_bf16(n, H, 15000 + seed)
+    wts = I.normal_weights(n, K, 16000 + seed)
+    g = ep.ep_create_group(mode=c["mode"], num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=H, max_tokens_per_rank=T, num_src_ranks=S, payload="fp8")
+    try:
+        topk_d = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, N, K, M))
+        h = ep.ep_create_handle(g, topk_d)
+        ep.ep_dispatch(h, x.cuda(), topk_weights=None if ll else dev(wts))
+        xb = I.bf16_bits(x)
+        if ll:
+            cnt, slot, _ = oracle.layout_ll(topk, S, E, T)
+            np.testing.assert_array_equal(get_map(h, A.EP_MAP_LL_COUNT), cnt)
+            np.testing.assert_array_equal(get_map(h, A.EP_MAP_LL_SLOT), slot)
+            used = np.unique(slot[slot >= 0])
+            dense = np.where(slot >= 0, np.searchsorted(used, slot), -1).astype(np.int32)
+            got = host(ep.ep_handle_get_buffer(h, A.EP_BUF_LL_RECV)[torch.from_numpy(used.astype(np.int64)).cuda()])
+            np.testing.assert_array_equal(got, oracle.pack_ll(xb, T, K, True, dense, len(used)))
+        else:
+            lay = oracle.layout_ht(topk, S, E, N, G)
+            for which, key in [(A.EP_MAP_HT_NODE_ROW, "node_row"), (A.EP_MAP_HT_ROW, "row2"),
+                               (A.EP_MAP_HT_RANK_COUNT, "c1"), (A.EP_MAP_HT_RANK_OFFSET, "off1"),
+                               (A.EP_MAP_HT_EXPERT_COUNT, "c2"), (A.EP_MAP_HT_EXPERT_OFFSET, "off2")]:
+                np.testing.assert_array_equal(get_map(h, which), lay[key], err_msg=key)
+            r1, r2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+            pk = oracle.pack_ht(xb, topk, wts, T, N, True, lay["node_row"], lay["row2"], r1, r2)
+            np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE1)[:r1]), pk["stage1"])
+            np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2)[:r2]), pk["stage2"])
+        assert ep.ep_get_device_error(g) == 0
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
