@@ -243,3 +243,56 @@ def test_random_large_batches_layout_and_rows(seed):
         ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("mode", ["ht", "ll"])
+def test_handle_slot_reuse_with_changing_batches(mode):
+    """Twelve handles in turn through a two-slot pool on one group, with the
+    batch growing and shrinking (1 .. T_max tokens per source, LL across the
+    one-launch and two-launch handle paths): every handle's maps, counts,
+    rows and combine equal the oracle's, so nothing of an earlier, larger
+    handle leaks into a later one."""
+    N, G, E, K, M, S, T_max, H = 4, 2, 64, 6, 2, 3, 400, 128
+    say(f"handle slot reuse {mode}")
+    g = ep.ep_create_group(mode=mode, num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=H, max_tokens_per_rank=T_max, num_src_ranks=S,
+                           payload="fp8", max_handles=2)
+    try:
+        for j, T in enumerate([400, 3, 257, 64, 1, 399, 130, 5, 256, 2, 300, 65]):
+            n = S * T
+            scores = I.uniform_scores(n, E, seed=17000 + j).astype(np.float32)
+            x = I.normal_bf16(n, H, 17100 + j)
+            wts = I.normal_weights(n, K, 17200 + j)
+            topk_d = torch.empty((n, K), dtype=torch.int32, device="cuda")
+            ep.ep_route(g, dev(scores), topk_d)
+            topk = host(topk_d)
+            h = ep.ep_create_handle(g, topk_d)
+            ep.ep_dispatch(h, x.cuda(), topk_weights=None if mode == "ll" else dev(wts))
+            xb = I.bf16_bits(x)
+            if mode == "ll":
+                cnt, loc, _ = oracle.layout_ll(topk, S, E, T_max)
+                np.testing.assert_array_equal(get_map(h, A.EP_MAP_LL_COUNT), cnt, err_msg=f"T={T}")
+                np.testing.assert_array_equal(get_map(h, A.EP_MAP_LL_SLOT), loc, err_msg=f"T={T}")
+                used = np.unique(loc[loc >= 0])
+                dense = np.where(loc >= 0, np.searchsorted(used, loc), -1).astype(np.int32)
+                got = host(ep.ep_handle_get_buffer(h, A.EP_BUF_LL_RECV)[torch.from_numpy(used.astype(np.int64)).cuda()])
+                np.testing.assert_array_equal(got, oracle.pack_ll(xb, T, K, True, dense, len(used)))
+                rows = E * S * T_max
+            else:
+                lay = oracle.layout_ht(topk, S, E, N, G)
+                for which, key in [(A.EP_MAP_HT_NODE_ROW, "node_row"), (A.EP_MAP_HT_ROW, "row2"),
+                                   (A.EP_MAP_HT_RANK_COUNT, "c1"), (A.EP_MAP_HT_RANK_OFFSET, "off1"),
+                                   (A.EP_MAP_HT_EXPERT_COUNT, "c2"), (A.EP_MAP_HT_EXPERT_OFFSET, "off2")]:
+                    np.testing.assert_array_equal(get_map(h, which), lay[key], err_msg=f"{key} T={T}")
+                r1, r2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+                pk = oracle.pack_ht(xb, topk, wts, T, N, True, lay["node_row"], lay["row2"], r1, r2)
+                np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2)[:r2]), pk["stage2"])
+                loc, rows = lay["row2"], r2
+            Y = I.normal_bf16(rows, H, 17300 + j)
+            out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+            ep.ep_combine(h, Y.cuda().view(E, S * T_max, H) if mode == "ll" else Y.cuda(), dev(wts), out)
+            np.testing.assert_array_equal(host(out), oracle.combine(I.bf16_bits(Y), wts, loc), err_msg=f"T={T}")
+            assert ep.ep_get_device_error(g) == 0
+            ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
