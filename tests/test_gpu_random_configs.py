@@ -296,3 +296,65 @@ def test_handle_slot_reuse_with_changing_batches(mode):
             ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+@pytest.mark.parametrize("seed", range(32))
+def test_random_prequantised_dispatch_and_partitions(seed):
+    """Random draws (FP8 groups): ep_quantize then a dispatch of the FP8
+    tokens with their scales writes exactly what the dispatch of the BF16
+    tokens writes, and ep_get_partition of random ranks is exactly that
+    rank's slice of the whole receive buffer."""
+    c = _draw(19000 + seed)
+    N, G, E, K, M, S, T = c["N"], c["G"], c["E"], c["K"], c["M"], c["S"], c["T"]
+    H = int(np.random.default_rng(seed).choice([128, 256, 512]))
+    ll, R, n = c["mode"] == "ll", N * G, S * T
+    say(f"random pre-quantised dispatch {seed}: {c} H={H}")
+    scores = I.uniform_scores(n, E, seed=19100 + seed).astype(np.float32)
+    x = I.normal_bf16(n, H, 19200 + seed)
+    wts = I.normal_weights(n, K, 19300 + seed)
+    images = []
+    for form in ("bf16", "fp8"):
+        g = ep.ep_create_group(mode=c["mode"], num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                               max_nodes_per_token=M, hidden=H, max_tokens_per_rank=T, num_src_ranks=S,
+                               payload="fp8")
+        try:
+            topk_d = torch.empty((n, K), dtype=torch.int32, device="cuda")
+            ep.ep_route(g, dev(scores), topk_d)
+            h = ep.ep_create_handle(g, topk_d)
+            w = None if ll else dev(wts)
+            if form == "bf16":
+                ep.ep_dispatch(h, x.cuda(), topk_weights=w)
+            else:
+                q = torch.empty((n, H), dtype=torch.float8_e4m3fn, device="cuda")
+                sc = torch.empty((n, H // 128), dtype=torch.float32, device="cuda")
+                ep.ep_quantize(g, x.cuda(), q, sc)
+                ep.ep_dispatch(h, q, scales=sc, topk_weights=w)
+            which = A.EP_BUF_LL_RECV if ll else A.EP_BUF_HT_STAGE2
+            whole = ep.ep_handle_get_buffer(h, which)
+            if ll:
+                loc = get_map(h, A.EP_MAP_LL_SLOT)
+                used = torch.from_numpy(np.unique(loc[loc >= 0]).astype(np.int64)).cuda()
+                images.append(host(whole[used]))
+            else:
+                r2 = ep.ep_handle_get_num_recv(h, -1)
+                images.append(host(whole[:r2]))
+            # partitions of a few ranks are slices of the whole buffer
+            per = E // R * S * T if ll else None
+            for r in sorted({0, R - 1, int(np.random.default_rng(seed + 5).integers(0, R))}):
+                part = ep.ep_get_partition(h, r, which)
+                if ll:
+                    first, count = r * per, per
+                else:
+                    offs = get_map(h, A.EP_MAP_HT_EXPERT_OFFSET)
+                    cnts = get_map(h, A.EP_MAP_HT_EXPERT_COUNT)
+                    L = E // R
+                    first, count = int(offs[r * L]), int(cnts[r * L:(r + 1) * L].sum())
+                assert part.shape[0] == count
+                if count:
+                    assert part.data_ptr() == whole[first].data_ptr()
+                    np.testing.assert_array_equal(host(part), host(whole[first:first + count]))
+            assert ep.ep_get_device_error(g) == 0
+            ep.ep_destroy_handle(h)
+        finally:
+            ep.ep_destroy_group(g)
+    np.testing.assert_array_equal(images[0], images[1])
