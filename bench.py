@@ -47,6 +47,7 @@ import ep_inputs as I  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 N_SETS = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ht_prefill_combine_4096.txt")
+TRAFFIC_FILE_ROUND_TRIP = os.path.join(ROOT, "profiles", "traffic_ht_round_trip_16384_zipf.txt")
 KERNEL_SOURCES = ("ep_dispatch.hip", "ep_combine.hip")
 
 
@@ -93,13 +94,13 @@ def source_digest():
     return h.hexdigest()[:16]
 
 
-def stored_traffic(kernel: str):
+def stored_traffic(kernel: str, path: str = TRAFFIC_FILE):
     """HBM bytes per launch measured with rocprofv3 PMC counters, if the
     stored measurement was taken on the current kernel sources."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     vals = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         line = line.strip()
         if line and not line.startswith("#") and "=" in line:
             k, v = line.split("=", 1)
@@ -275,7 +276,8 @@ def time_cpu_sync(ep, g, s, reps=50):
     return {"wait": q(wait), "route_handle_wait": q(full)}
 
 
-def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok, pct):
+def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok, pct,
+                traffic_file=TRAFFIC_FILE):
     names = ["route", "handle", "dispatch", "combine"]
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
     dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
@@ -312,7 +314,7 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
                        "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": stored_traffic(dom) if traffic_ok else None,
+                     "traffic": stored_traffic(dom, traffic_file) if traffic_ok else None,
                      "algorithmic_bytes_per_launch": ab[dom]},
     }
 
@@ -391,7 +393,8 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
               "stage1_rows": rows1, "stage2_rows": rows2, "algorithmic_bytes_per_step": ab["total"]}
     headline = not per_rank and node_limit == 4 and not round_trip
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
-                         traffic_ok=headline, pct=pct)
+                         traffic_ok=headline or round_trip, pct=pct,
+                         traffic_file=TRAFFIC_FILE_ROUND_TRIP if round_trip else TRAFFIC_FILE)
     result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
         result["dtype"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"

@@ -61,13 +61,28 @@ def test_stored_traffic_is_consistent():
 
 
 def test_cpu_baseline_object(monkeypatch):
-    """The oracle leg: one whole run of the 4096-token step on the host,
-    reported as the oracle with the threads it used and what it ran."""
+    """The oracle leg, on a 256-token batch of the prefill workload's shape:
+    one whole run on the host, reported as the oracle with the threads it
+    used, what it ran, and value = the step's algorithmic bytes / time."""
     import ep_inputs as I
+    import oracle
     monkeypatch.setattr(bench, "MIN_CPU_SECONDS", 0.0)
-    w = I.HT_PREFILL
-    cb = bench.cpu_baseline(I.scores_for(w), I.tokens_for(w), I.normal_weights(4096, 8, w.seed),
-                            I.normal_bf16(4096 * 8, 7168, I.COMBINE.seed), 4096)
+    n = 256
+    scores = I.page_scores(n, 256, 0)
+    w = I.normal_weights(n, 8, 0)
+    cb = bench.cpu_baseline(scores, I.normal_bf16(n, 7168, 1), w, I.normal_bf16(n * 8, 7168, 2), n)
     assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1 and cb["runs"] == 1
-    assert cb["value"] > 0 and "4096 tokens" in cb["sample"]
-    assert abs(cb["value"] - 955_810_496 / cb["seconds"] / 1e9) <= 0.01 * cb["value"]
+    assert cb["value"] > 0 and f"{n} tokens" in cb["sample"]
+    lay = oracle.layout_ht(oracle.route(scores, 8, 8, 4), 1, 256, 8, 8)
+    ab = bench.algorithmic_bytes(n, 8, 7168, int(lay["c1"].sum()), int(lay["c2"].sum()), 256)["total"]
+    # seconds is rounded to the millisecond
+    assert abs(cb["value"] - ab / cb["seconds"] / 1e9) <= cb["value"] * (0.01 + 0.0006 / cb["seconds"])
+
+
+def test_stored_round_trip_traffic_is_consistent():
+    # 16384 tokens, Zipf(1.1) routing (seed 5): 64,695 stage-1 and 131,072 stage-2 rows
+    ab = bench.algorithmic_bytes(16384, 8, 7168, 64695, 131072, 256)
+    for kernel in ("dispatch", "combine"):
+        t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_ROUND_TRIP)
+        if t is not None:
+            assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
