@@ -296,7 +296,10 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3 payload / bf16 combine, fp32 accumulate",
+        # the arithmetic type: quantisation and the combine's accumulation are
+        # fp32; FP8 and BF16 are the storage formats of rows and tokens
+        "dtype": "f32",
+        "formats": "fp8_e4m3 payload + fp32 scales / bf16 combine, fp32 accumulate",
         "data": "synthetic (seeded; the DeepEP routing study's score distribution, N(0,1) tokens and expert outputs)",
         "config": config,
         "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
@@ -397,7 +400,7 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
                          traffic_file=TRAFFIC_FILE_ROUND_TRIP if round_trip else TRAFFIC_FILE)
     result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
-        result["dtype"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
+        result["formats"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
     if round_trip:
         result["data"] = ("synthetic (seeded; U[0,1) scores plus a normalised Zipf(1.1) expert popularity, "
                           "N(0,1) tokens; the combine input is the identity expert's output of the "
@@ -474,7 +477,7 @@ def run_ll(args, ep, S, payload="fp8"):
               "algorithmic_bytes_per_step": ab["total"]}
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok=False, pct=pct)
     if payload != "fp8":
-        result["dtype"] = "bf16 payload / bf16 combine, fp32 accumulate"
+        result["formats"] = "bf16 payload / bf16 combine, fp32 accumulate"
     result["us_per_call"] = {k: round(float(v) * 1e3, 2)
                              for k, v in zip(["route", "handle", "dispatch", "combine"], mean_ms)}
     if not args.no_cpu_baseline and payload == "fp8":
@@ -543,7 +546,7 @@ def run_ht_backward(args, ep):
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "execution": args.mode,
         "ms_per_step_eager": round(ms_eager, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16 gradients, fp32 accumulate",
+        "vs_baseline": None, "dtype": "f32", "formats": "bf16 gradients, fp32 accumulate",
         "data": "synthetic (seeded; the DeepEP routing study's score distribution, N(0,1) gradients and expert outputs)",
         "config": {"workload": "ht_prefill_4096_backward", "tokens": n_tok, "hidden": H, "experts": E,
                    "top_k": K, "nodes": 8, "ranks_per_node": 8, "max_nodes_per_token": 4,

@@ -28,6 +28,7 @@ def test_bench_json_line():
     assert d["metric"] == "dispatch+combine HBM GB/s and tokens/s on 1 MI355X (% of HBM peak)"
     assert d["unit"] == "GB/s" and d["n_gpus"] == 1 and d["steps"] == 8 and d["warmup"] == 2
     assert d["higher_is_better"] is True and d["scaling"] == "weak" and d["vs_baseline"] is None
+    assert d["dtype"] == "f32" and d["data"].startswith("synthetic")
     assert d["config"]["workload"] == "ht_prefill_4096_plus_combine"
     ab = d["config"]["algorithmic_bytes_per_step"]
     assert ab == 955_810_496
