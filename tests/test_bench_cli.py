@@ -86,3 +86,11 @@ def test_stored_round_trip_traffic_is_consistent():
         t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_ROUND_TRIP)
         if t is not None:
             assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
+
+
+def test_stored_ll_traffic_is_consistent():
+    ab = bench.ll_algorithmic_bytes(8192, 8, 7168, 256, 64)
+    for kernel in ("dispatch", "combine"):
+        t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_LL)
+        if t is not None:
+            assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
