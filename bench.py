@@ -49,6 +49,7 @@ N_SETS = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ht_prefill_combine_4096.txt")
 TRAFFIC_FILE_ROUND_TRIP = os.path.join(ROOT, "profiles", "traffic_ht_round_trip_16384_zipf.txt")
 TRAFFIC_FILE_LL = os.path.join(ROOT, "profiles", "traffic_ll_decode_64x128.txt")
+TRAFFIC_FILE_BWD = os.path.join(ROOT, "profiles", "traffic_ht_backward_4096.txt")
 KERNEL_SOURCES = ("ep_dispatch.hip", "ep_combine.hip")
 
 
@@ -561,7 +562,8 @@ def run_ht_backward(args, ep):
         "kernel_gbs": {"combine_backward": round(cb / (mean_ms[0] * 1e-3) / 1e9, 1),
                        "dispatch_backward": round(db / (mean_ms[1] * 1e-3) / 1e9, 1)},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": stored_traffic(dom, TRAFFIC_FILE_BWD),
                      "algorithmic_bytes_per_launch": dom_b},
     }
     for s in sets:

@@ -94,3 +94,13 @@ def test_stored_ll_traffic_is_consistent():
         t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_LL)
         if t is not None:
             assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
+
+
+def test_stored_backward_traffic_is_consistent():
+    n, K, H, rows = 4096, 8, 7168, 32768
+    alg = {"combine_backward": n * H * 2 + 2 * rows * H * 2 + 3 * n * K * 4,
+           "dispatch_backward": rows * H * 2 + n * K * 4 + n * H * 2}
+    for kernel, b in alg.items():
+        t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_BWD)
+        if t is not None:
+            assert abs(t / b - 1) < 0.05, (kernel, t, b)
