@@ -1,0 +1,72 @@
+"""The CU cap (num_cus): dispatch, combine and the adjoints launch fewer
+workgroups and loop over the work; the results must not change.  GPU vs
+oracle, whole, in both modes and with caps from 1 to 17 CUs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import A, I, buffer, dev, ep, get_map, host, need_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    need_gpu()
+
+
+@pytest.mark.parametrize("mode", ["ht", "ll"])
+@pytest.mark.parametrize("num_cus", [1, 3, 17])
+def test_capped_launches_equal_the_oracle(mode, num_cus):
+    N, G, E, K, M, S, T, H = 4, 2, 64, 6, 2, 3, 300, 1024
+    n, ll = S * T, mode == "ll"
+    say(f"CU cap {num_cus} {mode}")
+    scores = I.uniform_scores(n, E, seed=21000 + num_cus).astype(np.float32)
+    x = I.normal_bf16(n, H, 21100 + num_cus)
+    wts = I.normal_weights(n, K, 21200 + num_cus)
+    g = ep.ep_create_group(mode=mode, num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=H, max_tokens_per_rank=T, num_src_ranks=S,
+                           payload="fp8", num_cus=num_cus)
+    try:
+        topk_d = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        ep.ep_route(g, dev(scores), topk_d)
+        topk = host(topk_d)
+        np.testing.assert_array_equal(topk, oracle.route(scores, N, K, M))
+        h = ep.ep_create_handle(g, topk_d)
+        ep.ep_dispatch(h, x.cuda(), topk_weights=None if ll else dev(wts))
+        xb = I.bf16_bits(x)
+        if ll:
+            _, loc, _ = oracle.layout_ll(topk, S, E, T)
+            used = np.unique(loc[loc >= 0])
+            dense = np.where(loc >= 0, np.searchsorted(used, loc), -1).astype(np.int32)
+            got = host(ep.ep_handle_get_buffer(h, A.EP_BUF_LL_RECV)[torch.from_numpy(used.astype(np.int64)).cuda()])
+            np.testing.assert_array_equal(got, oracle.pack_ll(xb, T, K, True, dense, len(used)))
+            rows, shape = E * S * T, (E, S * T, H)
+        else:
+            lay = oracle.layout_ht(topk, S, E, N, G)
+            loc = lay["row2"]
+            r1, r2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+            pk = oracle.pack_ht(xb, topk, wts, T, N, True, lay["node_row"], loc, r1, r2)
+            np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE1)[:r1]), pk["stage1"])
+            np.testing.assert_array_equal(host(buffer(g, A.EP_BUF_HT_STAGE2)[:r2]), pk["stage2"])
+            rows, shape = r2, (r2, H)
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_LL_SLOT if ll else A.EP_MAP_HT_ROW), loc)
+        Y = I.normal_bf16(rows, H, 21300 + num_cus)
+        Yd = Y.cuda().view(*shape)
+        out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine(h, Yd, dev(wts), out)
+        np.testing.assert_array_equal(host(out), oracle.combine(I.bf16_bits(Y), wts, loc))
+        gb = I.bf16_bits(I.normal_bf16(n, H, 21400 + num_cus))
+        dY = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+        ep.ep_combine_backward(h, torch.from_numpy(gb.view(np.int16)).view(torch.bfloat16).cuda(), dev(wts), dY)
+        want_dY, _, _ = oracle.combine_backward(gb, wts, loc, rows)
+        np.testing.assert_array_equal(host(dY.view(rows, H))[used if ll else slice(None)],
+                                      want_dY[used if ll else slice(None)])
+        gx = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+        ep.ep_dispatch_backward(h, Yd, gx)
+        np.testing.assert_array_equal(host(gx), oracle.dispatch_backward(I.bf16_bits(Y), loc))
+        assert ep.ep_get_device_error(g) == 0
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
