@@ -139,3 +139,40 @@ def test_allocator_hooks_on_the_device(mode):
     finally:
         ep.ep_destroy_group(g)
     assert pool.freed == pool.calls and not pool.live
+
+
+def test_side_stream_and_blocking_count_queries():
+    """The path enqueued on a non-default stream that is still busy with
+    earlier work: the blocking receive-count query and the partition query
+    wait for the handle's own stream, so they see the counts of this
+    routing."""
+    N, G, E, K, M, S, T = 8, 8, 256, 8, 4, 1, 4096
+    n = S * T
+    say("side stream, blocking queries behind earlier work")
+    scores = I.scores_for(I.HT_PREFILL)
+    want = oracle.layout_ht(oracle.route(scores, N, K, M), S, E, N, G)
+    g = ep.ep_create_group(mode="ht", num_nodes=N, ranks_per_node=G, num_experts=E, top_k=K,
+                           max_nodes_per_token=M, hidden=128, max_tokens_per_rank=T, num_src_ranks=S,
+                           payload="fp8")
+    try:
+        sc = dev(scores)
+        topk_d = torch.empty((n, K), dtype=torch.int32, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(side):
+            for _ in range(30):          # keep the side stream busy for several ms
+                big.fill_(7)
+            ep.ep_route(g, sc, topk_d)
+            h = ep.ep_create_handle(g, topk_d)
+            total = ep.ep_handle_get_num_recv(h, -1)
+            r5 = ep.ep_handle_get_num_recv(h, 5)
+            part = ep.ep_get_partition(h, 9, A.EP_BUF_HT_STAGE1)
+        assert total == int(want["c2"].sum())
+        assert r5 == int(want["c2"][5 * 4:6 * 4].sum())
+        assert part.shape[0] == want["c1"][9]
+        side.synchronize()
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
