@@ -49,6 +49,7 @@ N_SETS = 4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_ht_prefill_combine_4096.txt")
 TRAFFIC_FILE_ROUND_TRIP = os.path.join(ROOT, "profiles", "traffic_ht_round_trip_16384_zipf.txt")
 TRAFFIC_FILE_LL = os.path.join(ROOT, "profiles", "traffic_ll_decode_64x128.txt")
+TRAFFIC_FILE_LL_BF16 = os.path.join(ROOT, "profiles", "traffic_ll_decode_64x128_bf16.txt")
 TRAFFIC_FILE_BWD = os.path.join(ROOT, "profiles", "traffic_ht_backward_4096.txt")
 KERNEL_SOURCES = ("ep_dispatch.hip", "ep_combine.hip")
 
@@ -478,7 +479,8 @@ def run_ll(args, ep, S, payload="fp8"):
               "ranks_per_node": 8, "max_nodes_per_token": 4, "slots": T,
               "algorithmic_bytes_per_step": ab["total"]}
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
-                         traffic_ok=S == 64 and payload == "fp8", pct=pct, traffic_file=TRAFFIC_FILE_LL)
+                         traffic_ok=S == 64, pct=pct,
+                         traffic_file=TRAFFIC_FILE_LL if payload == "fp8" else TRAFFIC_FILE_LL_BF16)
     if payload != "fp8":
         result["formats"] = "bf16 payload / bf16 combine, fp32 accumulate"
     result["us_per_call"] = {k: round(float(v) * 1e3, 2)

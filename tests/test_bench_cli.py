@@ -88,10 +88,12 @@ def test_stored_round_trip_traffic_is_consistent():
             assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
 
 
-def test_stored_ll_traffic_is_consistent():
-    ab = bench.ll_algorithmic_bytes(8192, 8, 7168, 256, 64)
+@pytest.mark.parametrize("fp8", [True, False])
+def test_stored_ll_traffic_is_consistent(fp8):
+    ab = bench.ll_algorithmic_bytes(8192, 8, 7168, 256, 64, fp8=fp8)
+    path = bench.TRAFFIC_FILE_LL if fp8 else bench.TRAFFIC_FILE_LL_BF16
     for kernel in ("dispatch", "combine"):
-        t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_LL)
+        t = bench.stored_traffic(kernel, path)
         if t is not None:
             assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
 
