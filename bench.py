@@ -51,6 +51,8 @@ TRAFFIC_FILE_ROUND_TRIP = os.path.join(ROOT, "profiles", "traffic_ht_round_trip_
 TRAFFIC_FILE_LL = os.path.join(ROOT, "profiles", "traffic_ll_decode_64x128.txt")
 TRAFFIC_FILE_LL_BF16 = os.path.join(ROOT, "profiles", "traffic_ll_decode_64x128_bf16.txt")
 TRAFFIC_FILE_BWD = os.path.join(ROOT, "profiles", "traffic_ht_backward_4096.txt")
+TRAFFIC_FILE_PER_RANK = os.path.join(ROOT, "profiles", "traffic_ht_prefill_4096_per_rank.txt")
+TRAFFIC_FILE_NO_LIMIT = os.path.join(ROOT, "profiles", "traffic_ht_prefill_4096_no_node_limit.txt")
 KERNEL_SOURCES = ("ep_dispatch.hip", "ep_combine.hip")
 
 
@@ -398,9 +400,10 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
               "max_nodes_per_token": node_limit, "stage2": "per_rank" if per_rank else "per_expert",
               "stage1_rows": rows1, "stage2_rows": rows2, "algorithmic_bytes_per_step": ab["total"]}
     headline = not per_rank and node_limit == 4 and not round_trip
+    traffic_file = (TRAFFIC_FILE_ROUND_TRIP if round_trip else TRAFFIC_FILE_PER_RANK if per_rank
+                    else TRAFFIC_FILE_NO_LIMIT if node_limit == 0 else TRAFFIC_FILE)
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
-                         traffic_ok=headline or round_trip, pct=pct,
-                         traffic_file=TRAFFIC_FILE_ROUND_TRIP if round_trip else TRAFFIC_FILE)
+                         traffic_ok=True, pct=pct, traffic_file=traffic_file)
     result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
         result["formats"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"

@@ -106,3 +106,13 @@ def test_stored_backward_traffic_is_consistent():
         t = bench.stored_traffic(kernel, bench.TRAFFIC_FILE_BWD)
         if t is not None:
             assert abs(t / b - 1) < 0.05, (kernel, t, b)
+
+
+@pytest.mark.parametrize("rows1,rows2,per_rank,name", [(16248, 30574, True, "TRAFFIC_FILE_PER_RANK"),
+                                                       (21622, 32768, False, "TRAFFIC_FILE_NO_LIMIT")])
+def test_stored_prefill_variant_traffic_is_consistent(rows1, rows2, per_rank, name):
+    ab = bench.algorithmic_bytes(4096, 8, 7168, rows1, rows2, 256, per_rank)
+    for kernel in ("dispatch", "combine"):
+        t = bench.stored_traffic(kernel, getattr(bench, name))
+        if t is not None:
+            assert abs(t / ab[kernel] - 1) < 0.05, (kernel, t, ab[kernel])
