@@ -18,8 +18,9 @@
 //  2. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 (IEEE fp32 division)
 //     and q = E4M3(x/scale), the quotient by a refined reciprocal and one
-//     fused residual correction (equal to the IEEE quotient's codes on the
-//     whole bf16 domain, which the tests sweep).  Quantising comes before
+//     fused residual correction, on operands pre-scaled by 2^64 when the
+//     scale is tiny (the tests compare the codes with the IEEE quotient's
+//     for every finite bf16 amax).  Quantising comes before
 //     the positions, so the raw chunks' registers are free early.
 //  3. The token's rank inside its 64-token tile (from the handle) plus the
 //     tile's prefix gives every slot / row.  Positions are wave-uniform.
@@ -103,17 +104,27 @@ __device__ __forceinline__ void quantize(Raw& r) {
     float qv[16];
     // The quotient x/scale by Markstein's scheme: a Newton step refines the
     // hardware reciprocal, and one fused residual correction rounds the
-    // quotient.  The sign is copied from x afterwards, so -0 stays -0 as in
-    // the IEEE quotient.  Blocks whose scale is subnormal use the IEEE
-    // division.  Either way the quotient equals the IEEE one for every bf16
-    // input, and |quotient| <= 448 * (1 + 2^-8) < 464 (the saturation tie).
-    if (scale >= 1.17549435e-38f) {
-      float rinv = __builtin_amdgcn_rcpf(scale);
-      rinv = __builtin_fmaf(__builtin_fmaf(-scale, rinv, 1.0f), rinv, rinv);
+    // quotient.  The correction is exact only while the residual
+    // x - q0*scale is a normal fp32 number or a multiple of 2^-149; it is a
+    // multiple of about 2^-47 |x|, so that holds for |x| >= 2^-102.  Blocks
+    // with scale < 2^-64 therefore work on x*2^64 and scale*2^64 (both exact,
+    // the quotient unchanged): then every x whose code can be non-zero
+    // (|x| >= 2^-11 scale) is above 2^-89, and the scaled scale is a normal
+    // number for every bf16 amax down to the smallest subnormal.  The sign is
+    // copied from x afterwards, so -0 stays -0 as in the IEEE quotient, and
+    // |quotient| <= 448 * (1 + 2^-8) < 464 (the saturation tie).  An infinite
+    // amax (a block holding +-inf) takes the IEEE division: finite x give
+    // +-0 as x/inf does.
+    if (scale < __builtin_huge_valf()) {
+      const float k = scale < 0x1p-64f ? 0x1p64f : 1.0f;
+      const float ss = scale * k;
+      float rinv = __builtin_amdgcn_rcpf(ss);
+      rinv = __builtin_fmaf(__builtin_fmaf(-ss, rinv, 1.0f), rinv, rinv);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const float q0 = f[q] * rinv;
-        const float res = __builtin_fmaf(-q0, scale, f[q]);
+        const float xs = f[q] * k;
+        const float q0 = xs * rinv;
+        const float res = __builtin_fmaf(-q0, ss, xs);
         qv[q] = __builtin_copysignf(__builtin_fmaf(res, rinv, q0), f[q]);
       }
     } else {

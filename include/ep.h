@@ -302,6 +302,9 @@ ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *vi
  * With an FP8 payload each 128-element block is quantised as
  *   scale = amax/448 (fp32 division), q = E4M3(x/scale) (fp32 division,
  *   nearest-even, saturating), amax == 0 -> scale 0 and codes 0;
+ *   token values must be finite: in a block holding +-inf the scale is +inf
+ *   and the finite elements get the codes of x/inf (+-0), but the code of
+ *   an infinite or NaN element is unspecified;
  * row = [q: H bytes][scales: H/128 fp32] (7392 B at H = 7168).  A BF16
  * payload row is the H bf16 values (14336 B).
  *   LL message = row + 16-byte header int32 {src_token, src_rank, k, 0}
@@ -325,6 +328,8 @@ ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t *tokens,
  * the ones ep_dispatch writes when it quantises BF16 tokens itself:
  * scale = amax/448 per 128-element block, codes the nearest-even,
  * saturating E4M3 of x/scale; an all-zero block gets scale 0 and codes 0.
+ * Non-finite token values are handled as in ep_dispatch (the codes of
+ * infinite and NaN elements are unspecified).
  *   tokens: BF16 [n, H], rows 16-byte aligned, innermost contiguous.
  *   q:      FP8_E4M3 [n, H] out, rows 16-byte aligned.
  *   scales: F32 [n, H/128] out.

@@ -104,10 +104,12 @@ double orc_e4m3_value(int code)
 /* float -> E4M3: nearest representable value, ties to the even code, finite
  * magnitudes beyond 448 saturate to +-448, the sign of zero is kept.
  * The bracketing pair is found by bisection over the monotone code table;
- * the decision compares |v| with the exact midpoint (exact in double). */
+ * the decision compares |v| with the exact midpoint (exact in double).
+ * A NaN gets the format's NaN code S.1111.111 (its sign bit as it comes). */
 uint8_t orc_e4m3_encode(float v)
 {
     uint8_t sign = signbit(v) ? 0x80 : 0x00;
+    if (isnan(v)) return sign | 0x7F;
     double a = fabs((double)v);
     if (a >= 448.0) return sign | 0x7E;
     int lo = 0, hi = 126;              /* value(lo) <= a < value(hi) */

@@ -104,6 +104,40 @@ def test_e4m3_signed_zero_and_saturation():
     assert oracle.e4m3_encode(-1e6) == 0xFE
 
 
+def test_e4m3_nan_is_the_format_nan():
+    """A NaN encodes to S.1111.111, which torch's float8_e4m3fn reads as NaN
+    (the format has no infinities and one NaN pattern per sign)."""
+    pos = np.array([np.nan], np.float32)
+    neg = -pos
+    for v in (pos, neg):
+        c = int(oracle.e4m3_encode_array(v)[0])
+        assert c & 0x7F == 0x7F
+        assert c & 0x80 == (0x80 if np.signbit(v[0]) else 0)
+        assert np.isnan(torch.tensor([c], dtype=torch.uint8).view(torch.float8_e4m3fn).float().item())
+
+
+def test_block_with_infinity():
+    """A block holding +-inf: amax is inf, so scale = inf/448 = inf and every
+    finite x gives x/inf = +-0 (IEEE 754 division), codes 0x00 / 0x80; the
+    infinite element's quotient inf/inf is NaN, a NaN code.  The other block
+    of the row is unaffected."""
+    x = np.zeros((1, 256), np.float32)
+    x[0, :128] = np.linspace(-3.0, 3.0, 128, dtype=np.float32)
+    x[0, 17] = np.inf
+    x[0, 128:] = np.linspace(-1.0, 1.0, 128, dtype=np.float32)
+    bits = I.bf16_bits(torch.from_numpy(x).to(torch.bfloat16))
+    q, sc = oracle.quantize_rows(bits)
+    assert np.isinf(sc[0, 0]) and sc[0, 0] > 0
+    finite = np.ones(128, bool)
+    finite[17] = False
+    want = np.where(bits[0, :128] & 0x8000, 0x80, 0x00).astype(np.uint8)
+    np.testing.assert_array_equal(q[0, :128][finite], want[finite])
+    assert q[0, 17] & 0x7F == 0x7F
+    q2, sc2 = oracle.quantize_rows(bits[:, 128:].copy())
+    np.testing.assert_array_equal(q[0, 128:], q2[0])
+    assert sc[0, 1] == sc2[0, 0] == np.float32(1.0) / np.float32(448.0)
+
+
 # ---------------------------------------------------------------------------
 # Quantisation of rows: amax/448 scale, one per 128 elements
 # ---------------------------------------------------------------------------
