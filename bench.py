@@ -2,8 +2,8 @@
 """Benchmark: MoE EP dispatch + combine at the 4096-token DeepSeek-V3 shape on one MI355X.
 
 One step = the whole hot path over one batch, all inputs resident in HBM:
-  route    (A1)      scores [4096, 256] f32 -> topk_idx [4096, 8]
-  handle   (A2)      counts, prefix sums, stage-1 node rows, stage-2 rows
+  route_handle (A1+A2) scores [4096, 256] f32 -> topk_idx [4096, 8], then
+                     counts, prefix sums and in-tile ranks (one call)
   dispatch (A3+A5+A6) FP8 quantisation, node-deduplicated same-position
                      stage-1 rows and expert-grouped stage-2 rows (+ metadata)
   combine  (A7)      32768 expert-output rows (bf16, hidden 7168) gathered,
@@ -11,8 +11,9 @@ One step = the whole hot path over one batch, all inputs resident in HBM:
 Workload: 8 nodes x 8 ranks, 256 experts, top-8, at most 4 nodes per token,
 router scores U[0,1) + 0.5*U[0,1) per expert (seed 0) -- the DeepEP page's
 routing study; tokens and expert outputs ~N(0,1) bf16; weights softmax of
-N(0,1) logits.  Four input sets rotate so that no step reads what the
-previous one left in the last-level cache.
+N(0,1) logits.  Four input sets (scores, tokens, expert outputs, outputs)
+rotate so that no step reads what the previous one left in the last-level
+cache.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--mode graph|eager]
@@ -22,7 +23,9 @@ previous one left in the last-level cache.
 Prints one JSON line (rank 0).  value = algorithmic bytes of one step /
 step time, in GB/s, with the step time from one replay of a HIP graph that
 holds exactly K captured steps; tokens/s and the fraction of the 8 TB/s HBM
-peak are reported beside it.  The roofline object describes the dominant
+peak are reported beside it.  The default run also times the 64 x 128-token
+LL decode and the 16384-token skewed round trip the same way and adds them
+under "secondary" (value stays the 4096-token step's).  The roofline object describes the dominant
 kernel with its own average duration from HIP events recorded on the launch
 stream.  The other workloads (LL decode, per-rank stage 2, backward) report
 the same fields for their own steps.
@@ -63,9 +66,8 @@ def log(*a):
 def algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank=False):
     """Bytes each step must move at least once (read + write), per kernel.
 
-    route    : scores n*E*4 read, topk n*K*4 written
-    handle   : topk n*K*4 read; node rows n*N*4 and stage-2 rows n*K*4 written
-               (counted under dispatch in the headline total, as read there)
+    route_handle : scores n*E*4 read, topk n*K*4 written (the handle's own
+               counts and in-tile ranks are not counted)
     dispatch : tokens n*H*2 read, topk + weights 2*n*K*4 read,
                stage-1 rows1*(H + H/128*4) + metadata rows1*(2 + 2K)*4,
                stage-2 rows2*(H + H/128*4) + metadata rows2*3*4 written
@@ -82,7 +84,7 @@ def algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank=False):
     combine = rows2 * H * 2 + (1 if per_rank else 2) * n_tok * K * 4 + n_tok * H * 2
     # headline total = scores + tokens + topk + weights + stage rows/meta + combine
     total = n_tok * E * 4 + dispatch + combine
-    return dict(route=route, dispatch=dispatch, combine=combine, total=total)
+    return dict(route_handle=route, dispatch=dispatch, combine=combine, total=total)
 
 
 def source_digest():
@@ -116,40 +118,91 @@ def stored_traffic(kernel: str, path: str = TRAFFIC_FILE):
     return float(v) if v else None
 
 
-MIN_CPU_SECONDS = 10.0   # the oracle runs at least this long (whole runs)
+MIN_CPU_SECONDS = 8.0   # each leg of the CPU baseline runs at least this long (whole runs)
+
+
+def host_threads():
+    """Host threads the multi-core oracle leg uses: the CPUs this process may
+    run on, capped by OMP_NUM_THREADS when it is set (the GPU machine sets it to
+    its CPU share)."""
+    avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    return max(1, min(avail, cap) if cap > 0 else avail)
+
+
+def oracle_step(oracle, scores, xb, weights, yb, n_tok, pool, parts):
+    """One pass of the whole step through the oracle.  Routing, packing and
+    the combine are per token, so with a thread pool they run on disjoint
+    token ranges at once (the oracle's C functions release the interpreter
+    lock); the counting sort of the layout is one sequential pass.  Returns
+    (seconds of the timed parts, rows1, rows2)."""
+    def each(fn):
+        if pool is None:
+            return [fn(a, b) for a, b in parts]
+        return list(pool.map(lambda ab: fn(*ab), parts))
+    t0 = time.perf_counter()
+    topk = np.empty((n_tok, 8), np.int32)
+    def route(a, b):
+        topk[a:b] = oracle.route(scores[a:b], 8, 8, 4)
+    each(route)
+    lay = oracle.layout_ht(topk, 1, 256, 8, 8)
+    rows1, rows2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+    pk = oracle.pack_ht(xb[:0], topk[:0], weights[:0], n_tok, 8, True, lay["node_row"][:0], lay["row2"][:0],
+                        rows1, rows2)
+    def pack(a, b):
+        oracle.pack_ht(xb[a:b], topk[a:b], weights[a:b], n_tok, 8, True, lay["node_row"][a:b],
+                       lay["row2"][a:b], rows1, rows2, out=pk, first_token=a)
+    each(pack)
+    t1 = time.perf_counter()
+    y = oracle.dequant_rows(pk["stage2"], 7168, True) if yb is None else yb   # identity expert, untimed
+    del pk
+    t2 = time.perf_counter()
+    def comb(a, b):
+        oracle.combine(y, weights, lay["row2"], which=np.arange(a, b))
+    each(comb)
+    return (t1 - t0) + (time.perf_counter() - t2), rows1, rows2
 
 
 def cpu_baseline(scores, x, weights, Y, n_tok):
-    """The oracle on the same workload (all n_tok tokens), single thread,
-    repeated whole until MIN_CPU_SECONDS have passed.  Y None: the combine
-    takes the identity expert's output of the oracle's own stage-2 rows,
-    which is made outside the timed parts, as on the GPU."""
+    """The oracle on the same workload (all n_tok tokens), repeated whole
+    until MIN_CPU_SECONDS have passed: on all the host threads this process
+    may use (token ranges in parallel; `value`), and single-threaded.  Y None:
+    the combine takes the identity expert's output of the oracle's own
+    stage-2 rows, made outside the timed parts, as on the GPU."""
     import oracle
+    from concurrent.futures import ThreadPoolExecutor
     xb = I.bf16_bits(x)
     yb = None if Y is None else I.bf16_bits(Y)
-    runs, busy = 0, 0.0
-    while True:
-        t0 = time.perf_counter()
-        topk = oracle.route(scores, 8, 8, 4)
-        lay = oracle.layout_ht(topk, 1, 256, 8, 8)
-        rows1, rows2 = int(lay["c1"].sum()), int(lay["c2"].sum())
-        pk = oracle.pack_ht(xb, topk, weights, n_tok, 8, True, lay["node_row"], lay["row2"], rows1, rows2)
-        t1 = time.perf_counter()
-        y = oracle.dequant_rows(pk["stage2"], 7168, True) if Y is None else yb
-        del pk
-        t2 = time.perf_counter()
-        oracle.combine(y, weights, lay["row2"])
-        busy += (t1 - t0) + (time.perf_counter() - t2)
-        runs += 1
-        if busy >= MIN_CPU_SECONDS:
-            break
-    dt = busy / runs
+    threads = host_threads()
+    legs = {}
+    for name, nthr in (("all_cores", threads), ("single_thread", 1)):
+        parts = [(int(a), int(b)) for a, b in zip(np.linspace(0, n_tok, nthr + 1)[:-1],
+                                                  np.linspace(0, n_tok, nthr + 1)[1:]) if b > a]
+        pool = ThreadPoolExecutor(nthr) if nthr > 1 else None
+        runs, busy = 0, 0.0
+        try:
+            while True:
+                dt, rows1, rows2 = oracle_step(oracle, scores, xb, weights, yb, n_tok, pool, parts)
+                busy += dt
+                runs += 1
+                if busy >= MIN_CPU_SECONDS:
+                    break
+        finally:
+            if pool:
+                pool.shutdown()
+        legs[name] = (busy / runs, runs, nthr)
     b = algorithmic_bytes(n_tok, 8, 7168, rows1, rows2, 256)["total"]
     expert = " (identity expert untimed)" if Y is None else ""
-    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=1, kind="oracle",
+    dt, runs, nthr = legs["all_cores"]
+    dt1, runs1, _ = legs["single_thread"]
+    return dict(value=round(b / dt / 1e9, 4), unit="GB/s", cores=nthr, kind="oracle",
                 sample=f"the whole step workload ({n_tok} tokens: route, layout, FP8 quantise + HT pack, "
-                       f"combine{expert}), run {runs} times, {dt:.2f} s per run single-threaded",
-                seconds=round(dt, 3), runs=runs, tokens_per_s=round(n_tok / dt, 1))
+                       f"combine{expert}); per-token stages on {nthr} threads over token ranges, the layout's "
+                       f"counting sort on one; {runs} runs of {dt:.2f} s",
+                seconds=round(dt, 3), runs=runs, tokens_per_s=round(n_tok / dt, 1),
+                nproc=os.cpu_count(), affinity=len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else None,
+                single_thread={"value": round(b / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                               "seconds": round(dt1, 3), "runs": runs1, "tokens_per_s": round(n_tok / dt1, 1)})
 
 
 def ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=True):
@@ -165,7 +218,7 @@ def ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=True):
     dispatch = n_tok * H * 2 + 2 * n_tok * K * 4 + E * S * 4 + n_tok * K * msg
     combine = n_tok * K * H * 2 + 2 * n_tok * K * 4 + n_tok * H * 2
     total = n_tok * E * 4 + dispatch + combine
-    return dict(route=route, dispatch=dispatch, combine=combine, total=total)
+    return dict(route_handle=route, dispatch=dispatch, combine=combine, total=total)
 
 
 def ll_cpu_baseline(T=128):
@@ -202,7 +255,7 @@ def ll_cpu_baseline(T=128):
                 seconds=round(dt, 3), sources=done, tokens_per_s=round(T * done / dt, 1))
 
 
-def time_steps(step, args, stream, out_of, ep, g, n_calls=4):
+def time_steps(step, args, stream, out_of, ep, g, n_calls=3):
     """Warm-up, an eager pass with events around every call (per-call ms),
     then (graph mode) one captured step per input set, replayed; the graph's
     output must equal the eager output of the same step."""
@@ -268,8 +321,7 @@ def time_cpu_sync(ep, g, s, reps=50):
     for _ in range(reps):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        ep.ep_route(g, s["scores"], s["topk"])
-        h = ep.ep_create_handle(g, s["topk"])
+        h = ep.ep_route_handle(g, s["scores"], s["topk"])
         ep.ep_handle_get_num_recv(h, -1)
         t1 = time.perf_counter()
         ep.ep_handle_get_num_recv(h, -1)
@@ -281,13 +333,17 @@ def time_cpu_sync(ep, g, s, reps=50):
     return {"wait": q(wait), "route_handle_wait": q(full)}
 
 
+STEP_CALLS = ["route_handle", "dispatch", "combine"]
+
+
 def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok, pct,
                 traffic_file=TRAFFIC_FILE):
-    names = ["route", "handle", "dispatch", "combine"]
+    names = STEP_CALLS
+    ms = dict(zip(names, mean_ms))
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
-    dom = "combine" if mean_ms[3] >= mean_ms[2] else "dispatch"
-    dom_ms = mean_ms[names.index(dom)]
-    achieved = ab[dom] / (dom_ms * 1e-3) / 1e9
+    dom = "combine" if ms["combine"] >= ms["dispatch"] else "dispatch"
+    achieved = ab[dom] / (ms[dom] * 1e-3) / 1e9
+    i_d, i_c = names.index("dispatch"), names.index("combine")
     return {
         "metric": "dispatch+combine HBM GB/s and tokens/s on 1 MI355X (% of HBM peak)",
         "value": round(value, 2),
@@ -309,22 +365,28 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
         "config": config,
         "tokens_per_s": round(n_tok / (ms_per_step * 1e-3), 1),
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
-        "kernel_ms": {k: round(float(v), 5) for k, v in zip(names, mean_ms)},
+        "kernel_ms": {k: round(float(v), 5) for k, v in ms.items()},
         "kernel_ms_percentiles": percentiles_ms(names, pct),
         # dispatch + combine alone at their median per-call times (route and
         # handle excluded): tokens / (t_dispatch + t_combine) and the bytes of
         # the two over the same time
         "dispatch_combine_median": {
-            "tokens_per_s": round(n_tok / ((pct[50][2] + pct[50][3]) * 1e-3), 1),
-            "gbs": round((ab["dispatch"] + ab["combine"]) / ((pct[50][2] + pct[50][3]) * 1e-3) / 1e9, 1)},
-        "kernel_gbs": {"route": round(ab["route"] / (mean_ms[0] * 1e-3) / 1e9, 1),
-                       "dispatch": round(ab["dispatch"] / (mean_ms[2] * 1e-3) / 1e9, 1),
-                       "combine": round(ab["combine"] / (mean_ms[3] * 1e-3) / 1e9, 1)},
+            "tokens_per_s": round(n_tok / ((pct[50][i_d] + pct[50][i_c]) * 1e-3), 1),
+            "gbs": round((ab["dispatch"] + ab["combine"]) / ((pct[50][i_d] + pct[50][i_c]) * 1e-3) / 1e9, 1)},
+        "kernel_gbs": {k: round(ab[k] / (ms[k] * 1e-3) / 1e9, 1) for k in names},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": stored_traffic(dom, traffic_file) if traffic_ok else None,
                      "algorithmic_bytes_per_launch": ab[dom]},
     }
+
+
+def secondary_line(r):
+    """The compact form of another workload's result line."""
+    return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"], "gbs": r["value"],
+            "frac_of_hbm_peak": r["frac_of_hbm_peak"], "tokens_per_s": r["tokens_per_s"],
+            "algorithmic_bytes_per_step": r["config"]["algorithmic_bytes_per_step"],
+            "kernel_ms": r["kernel_ms"], "roofline": r["roofline"]}
 
 
 def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
@@ -344,12 +406,14 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
     dev = torch.device("cuda")
     sets = []
     for j in range(N_SETS):
-        # every set holds the same values in different memory
+        # every set holds the same values in different memory, the expert
+        # outputs included (470 MB each at the prefill shape)
         sets.append(dict(scores=torch.from_numpy(scores).to(dev), x=x.to(dev),
                          topk=torch.empty((n_tok, K), dtype=torch.int32, device=dev),
-                         out=torch.empty((n_tok, H), dtype=torch.bfloat16, device=dev)))
+                         out=torch.empty((n_tok, H), dtype=torch.bfloat16, device=dev),
+                         Y=None if Y is None else Y.to(dev)))
     w_d = torch.from_numpy(weights).to(dev)
-    Y_d = None if Y is None else Y.to(dev)
+    Y_d = None
 
     g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=E, top_k=K,
                            max_nodes_per_token=node_limit, hidden=H, max_tokens_per_rank=n_tok,
@@ -362,23 +426,19 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
         s = sets[j % N_SETS]
         if ev is not None:
             ev[0].record(stream)
-        ep.ep_route(g, s["scores"], s["topk"])
+        h = ep.ep_route_handle(g, s["scores"], s["topk"])
         if ev is not None:
             ev[1].record(stream)
-        h = ep.ep_create_handle(g, s["topk"])
-        if ev is not None:
-            ev[2].record(stream)
         ep.ep_dispatch(h, s["x"], topk_weights=w_d)
         if ev is not None:
-            ev[3].record(stream)
-        ep.ep_combine(h, Y_d, w_comb, s["out"])
+            ev[2].record(stream)
+        ep.ep_combine(h, s["Y"] if s["Y"] is not None else Y_d, w_comb, s["out"])
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
         ep.ep_destroy_handle(h)
 
     # Exact row counts of this routing (the same every step).
-    ep.ep_route(g, sets[0]["scores"], sets[0]["topk"])
-    h = ep.ep_create_handle(g, sets[0]["topk"])
+    h = ep.ep_route_handle(g, sets[0]["scores"], sets[0]["topk"])
     rows2 = ep.ep_handle_get_num_recv(h, -1)
     rows1 = int(ep.ep_handle_get_map(h, ep._abi.EP_MAP_HT_RANK_COUNT).sum().item())
     if round_trip:
@@ -458,20 +518,17 @@ def run_ll(args, ep, S, payload="fp8"):
         s = sets[j % N_SETS]
         if ev is not None:
             ev[0].record(stream)
-        ep.ep_route(g, s["scores"], s["topk"])
+        h = ep.ep_route_handle(g, s["scores"], s["topk"])
         if ev is not None:
             ev[1].record(stream)
-        h = ep.ep_create_handle(g, s["topk"])
-        if ev is not None:
-            ev[2].record(stream)
         ep.ep_dispatch(h, s["x"], recv_counts=s["counts"], send_only=True)
         ep.ep_complete(h)
         if ev is not None:
-            ev[3].record(stream)
+            ev[2].record(stream)
         ep.ep_combine(h, Y_d, w_d, s["out"], send_only=True)
         ep.ep_complete(h)
         if ev is not None:
-            ev[4].record(stream)
+            ev[3].record(stream)
         ep.ep_destroy_handle(h)
 
     ab = ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=payload == "fp8")
@@ -486,8 +543,7 @@ def run_ll(args, ep, S, payload="fp8"):
                          traffic_file=TRAFFIC_FILE_LL if payload == "fp8" else TRAFFIC_FILE_LL_BF16)
     if payload != "fp8":
         result["formats"] = "bf16 payload / bf16 combine, fp32 accumulate"
-    result["us_per_call"] = {k: round(float(v) * 1e3, 2)
-                             for k, v in zip(["route", "handle", "dispatch", "combine"], mean_ms)}
+    result["us_per_call"] = {k: round(float(v) * 1e3, 2) for k, v in zip(STEP_CALLS, mean_ms)}
     if not args.no_cpu_baseline and payload == "fp8":
         log("[bench] timing the CPU oracle on one source's share")
         result["cpu_baseline"] = ll_cpu_baseline(T)
@@ -583,6 +639,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="with the default workload, skip the LL decode and round-trip lines")
     ap.add_argument("--num-cus", type=int, default=0, help="CU cap for dispatch/combine (0 = all)")
     ap.add_argument("--mode", choices=["graph", "eager"], default="graph",
                     help="graph: the step is captured once per input set in a HIP graph and replayed; "
@@ -626,6 +684,16 @@ def main(argv=None):
     if args.workload in ("ht_prefill", "ht_prefill_rank", "ht_prefill_nolimit"):
         result = run_ht(args, ep, per_rank=args.workload == "ht_prefill_rank",
                         node_limit=0 if args.workload == "ht_prefill_nolimit" else 4)
+        if args.workload == "ht_prefill" and not args.no_secondary:
+            # the LL decode and the skewed round trip, timed the same way on
+            # the same GPU; value stays the headline's
+            sub = argparse.Namespace(**{**vars(args), "no_cpu_baseline": True})
+            result["secondary"] = {}
+            for key, fn in (("ll_decode_64x128", lambda: run_ll(sub, ep, 64)),
+                            ("round_trip_16384_zipf", lambda: run_ht(sub, ep, w=I.ROUND_TRIP))):
+                torch.cuda.empty_cache()
+                result["secondary"][key] = secondary_line(fn())
+            torch.cuda.empty_cache()
     elif args.workload == "round_trip":
         result = run_ht(args, ep, w=I.ROUND_TRIP)
     elif args.workload == "ht_backward":

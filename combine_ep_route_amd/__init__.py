@@ -12,5 +12,6 @@ from .ep import (  # noqa: F401
     ep_create_handle, ep_dispatch_backward,
     ep_dequantize_rows, ep_destroy_group, ep_destroy_handle, ep_dispatch,
     ep_get_buffer, ep_get_device_error, ep_get_partition, ep_group_stats, ep_handle_get_buffer, ep_handle_get_map,
-    ep_handle_get_num_recv, ep_last_hip_error, ep_quantize, ep_route, ep_status_string, make_config,
+    ep_handle_get_num_recv, ep_last_hip_error, ep_quantize, ep_route, ep_route_handle, ep_status_string,
+    make_config,
 )

@@ -125,6 +125,7 @@ SIGNATURES = {
     "ep_group_stats": (_S, [_P, ctypes.POINTER(EpStats)]),
     "ep_route": (_S, [_P, _PT, _PT, _P]),
     "ep_create_handle": (_S, [_P, _PT, _P, ctypes.POINTER(_P)]),
+    "ep_route_handle": (_S, [_P, _PT, _PT, _P, ctypes.POINTER(_P)]),
     "ep_destroy_handle": (_S, [_P]),
     "ep_handle_get_num_recv": (_S, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "ep_handle_get_map": (_S, [_P, ctypes.c_int32, _PT]),

@@ -22,8 +22,9 @@
 //     scale is tiny (the tests compare the codes with the IEEE quotient's
 //     for every finite bf16 amax).  Quantising comes before
 //     the positions, so the raw chunks' registers are free early.
-//  3. The token's rank inside its 64-token tile (from the handle) plus the
-//     tile's prefix gives every slot / row.  Positions are wave-uniform.
+//  3. The token's rank inside its tile (from the handle) plus the tile's
+//     prefix (plus, in HT, the key's first row) gives every slot / row.
+//     Positions are wave-uniform.
 //  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
 //     size rounded up to 128 B).  Each chunk of codes goes to every
 //     destination row with non-temporal stores (nothing on this GPU reads
@@ -261,14 +262,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
         if (re >= 0) {
           const int key = (HT && p.s2_rank) ? me[k] / p.L : me[k];
           const int pre = p.hist_e[static_cast<int64_t>(j) * p.E2 + key] + re;
-          pos[k] = HT ? pre : (me[k] * p.S + s) * p.slots + pre;
+          pos[k] = HT ? p.off2[key] + pre : (me[k] * p.S + s) * p.slots + pre;
         }
       }
     }
     // Stage-1 row of destination node n (uniform), or -1.
     auto node_pos = [&](int n) -> int {
       if (!((my_nodes >> n) & 1)) return -1;
-      return p.hist_n[static_cast<int64_t>(j) * N + n] + p.rank_n[i * N + n];
+      return p.off1[n * p.G + s % p.G] + p.hist_n[static_cast<int64_t>(j) * N + n] + p.rank_n[i * N + n];
     };
 
     // 3. The handle's maps (written by the token's first wave).

@@ -20,7 +20,7 @@ constexpr int kMaxTopK = 32;
 constexpr int kMaxNodes = 64;
 constexpr int kMaxRanks = 1024;
 constexpr int kMaxHidden = 16384;
-constexpr int kLayoutTile = 64;    // tokens per layout tile (one wave)
+constexpr int kLayoutTile = 16;    // tokens per layout tile (one workgroup of the count kernel)
 
 constexpr uint32_t kGroupMagic = 0x45504752u;   // "EPGR"
 constexpr uint32_t kHandleMagic = 0x4550484Eu;  // "EPHN"
@@ -80,7 +80,8 @@ struct Group {
   int32_t* m2_k = nullptr;
   int32_t* m2_topk = nullptr;   // per-rank stage 2 only
   float* m2_w = nullptr;
-  int32_t* err = nullptr;
+  int32_t* err = nullptr;    // device error word
+  int32_t* done = nullptr;   // HT prefix scan: its workgroups finished (0 between launches)
 
   std::vector<Handle*> handles;
 
@@ -145,7 +146,11 @@ struct RouteArgs {
 hipError_t launch_route(const RouteArgs& a, hipStream_t stream);
 
 struct LayoutArgs {
-  const int32_t* topk;   // [n, K]
+  const int32_t* topk;   // [n, K], or null when the handle is made from scores
+  const float* scores;   // [n, E] with row stride ld, or null: route in the same pass
+  int64_t ld;
+  int M, J;              // routing: nodes kept (0 = no limit), scores summed per node
+  int32_t* topk_out;     // routing: the caller's [n, K] output
   int64_t n;
   int S, T, K, E, N, G, P;
   int slots;             // LL slots per (expert, source)
@@ -155,7 +160,6 @@ struct LayoutArgs {
   int s2_rank;           // HT stage 2 per (token, rank): key = e / L, first entry only
   int l_shift, p_shift;  // log2 of L and P when powers of two, else -1
   int tps, n_tiles;
-  int ll_fused;          // LL, one workgroup per source: the count kernel also writes the prefixes and counts
   int32_t* hist_e;
   int32_t* hist_n;
   int32_t* topk_copy;    // [n, K]
@@ -170,12 +174,9 @@ struct LayoutArgs {
   int32_t* c2;
   int32_t* off2;
   int32_t* err;
+  int32_t* done;         // HT scan: workgroups finished (zero between launches)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
-
-// LDS bytes the HT prefix-scan workgroup needs for S sources of tps tiles
-// (E = the stage-2 key count).
-size_t layout_scan_lds_bytes(int E, int N, int G, int S, int tps);
 
 // Receive stage of a dispatch: copy the [E, S] counters to out, or with
 // per_expert != 0 write their sums over S ([E]).
@@ -194,7 +195,7 @@ struct DispatchArgs {
   int in_fp8;             // tokens arrive quantised
   int out_fp8;            // payload is FP8
   int64_t n;
-  int T, K, N, H, E, S, P, slots, tps;
+  int T, K, N, G, H, E, S, P, slots, tps;
   int E2, L, s2_rank;     // stage-2 keys (E, or R per rank), experts per rank, per-rank flag
   int64_t row_bytes, msg_bytes;
   int64_t row_pitch, msg_pitch;   // strides of HT rows / LL messages in the buffers
@@ -207,6 +208,8 @@ struct DispatchArgs {
   const int32_t* rank_n;  // in-tile node ranks [n, N]
   const int32_t* hist_e;  // tile prefixes [tiles, E]
   const int32_t* hist_n;  // [tiles, N]
+  const int32_t* off1;    // HT: first stage-1 row of each rank [R]
+  const int32_t* off2;    // HT: first stage-2 row of each key [E2]
   int32_t* slot_map;      // LL out [n, K]
   int32_t* row2;          // HT out [n, K]
   int32_t* node_row;      // HT out [n, N]

@@ -140,7 +140,7 @@ ep_status_t ensure_device(Group* g, hipStream_t stream) {
   if (g->dev_ready) return EP_OK;
   EP_HIP(hipGetDevice(&g->device));
   EP_HIP(hipDeviceGetAttribute(&g->num_cu, hipDeviceAttributeMultiprocessorCount, g->device));
-  EP_HIP(launch_fill_i32(g->err, 1, 0, stream));
+  EP_HIP(launch_fill_i32(g->err, 2, 0, stream));   // the error word and the scan counter
   g->dev_ready = true;
   return EP_OK;
 }
@@ -185,6 +185,7 @@ DispatchArgs dispatch_base(const Handle* h) {
   p.T = h->T;
   p.K = g->cfg.top_k;
   p.N = g->cfg.num_nodes;
+  p.G = g->cfg.ranks_per_node;
   p.H = g->cfg.hidden;
   p.E = g->cfg.num_experts;
   p.S = g->cfg.num_src_ranks;
@@ -206,6 +207,8 @@ DispatchArgs dispatch_base(const Handle* h) {
   p.rank_n = h->rank_n;
   p.hist_e = h->hist_e;
   p.hist_n = h->hist_n;
+  p.off1 = h->off1;
+  p.off2 = h->off2;
   p.slot_map = h->slot_map;
   p.row2 = h->row2;
   p.node_row = h->node_row;
@@ -302,10 +305,6 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
     return EP_ERR_UNSUPPORTED;
   const bool s2_rank = cfg.mode == EP_MODE_HT && cfg.ht_stage2 == EP_HT_STAGE2_PER_RANK;
   const int E2 = s2_rank ? static_cast<int>(R) : E;
-  if (cfg.mode == EP_MODE_HT &&
-      layout_scan_lds_bytes(E2, N, cfg.ranks_per_node, cfg.num_src_ranks,
-                            (cfg.max_tokens_per_rank + kLayoutTile - 1) / kLayoutTile) > 65536)
-    return EP_ERR_UNSUPPORTED;   // more tiles than one workgroup's prefix scan holds
   if (cfg.max_handles == 0) cfg.max_handles = 2;
   if (cfg.ll_buffers == 0) cfg.ll_buffers = 2;
   if (cfg.max_handles > 64) return EP_ERR_UNSUPPORTED;
@@ -380,7 +379,10 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
       }
     }
   }
-  if (st == EP_OK) g->err = static_cast<int32_t*>(dev_alloc(g, sizeof(int32_t), &st));
+  if (st == EP_OK) {
+    g->err = static_cast<int32_t*>(dev_alloc(g, 2 * sizeof(int32_t), &st));
+    g->done = g->err ? g->err + 1 : nullptr;
+  }
   for (int hs = 0; st == EP_OK && hs < cfg.max_handles; ++hs) {
     const size_t nm = static_cast<size_t>(g->n_max);
     const size_t tiles = static_cast<size_t>(g->tiles_max);
@@ -510,15 +512,14 @@ EP_API ep_status_t ep_route(ep_group_t group, const ep_tensor_t* scores, ep_tens
 // Handles
 // ===========================================================================
 
-EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_idx, ep_stream_t stream,
-                                    ep_handle_t* out) {
-  Group* g = reinterpret_cast<Group*>(group);
-  if (!group_ok(g) || !out) return EP_ERR_INVALID_ARGUMENT;
-  *out = nullptr;
+namespace {
+
+// Takes a free handle slot and enqueues A2 for n = S*T tokens, from topk
+// (a caller's [n, K]) or, with scores, routing them into topk_out first in
+// the same pass (A1).
+ep_status_t make_handle(Group* g, const int32_t* topk, const float* scores, int64_t ld, int32_t* topk_out,
+                        int64_t n, hipStream_t s, ep_handle_t* out) {
   const int K = g->cfg.top_k, S = g->cfg.num_src_ranks;
-  if (!check2d(topk_idx, EP_DTYPE_I32, -1, K, EP_TAG_TOPK_IDX, false) || !contiguous2d(topk_idx))
-    return EP_ERR_INVALID_ARGUMENT;
-  const int64_t n = topk_idx->sizes[0];
   if (n % S != 0) return EP_ERR_INVALID_ARGUMENT;
   const int64_t T = n / S;
   if (T > g->cfg.max_tokens_per_rank) return EP_ERR_CAPACITY;
@@ -526,7 +527,6 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   for (Handle* c : g->handles)
     if (!c->in_use) { h = c; break; }
   if (!h) return EP_ERR_CAPACITY;
-  const hipStream_t s = as_stream(stream);
   if (const ep_status_t st = ensure_device(g, s); st != EP_OK) return st;
 
   h->n = n;
@@ -535,7 +535,12 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   h->n_tiles = h->tps * S;
   h->stream = s;
   LayoutArgs a{};
-  a.topk = static_cast<const int32_t*>(topk_idx->data);
+  a.topk = topk;
+  a.scores = scores;
+  a.ld = ld;
+  a.M = g->M;
+  a.J = g->J;
+  a.topk_out = topk_out;
   a.n = n;
   a.S = S;
   a.T = h->T;
@@ -567,6 +572,7 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   a.c2 = h->c2;
   a.off2 = h->off2;
   a.err = g->err;
+  a.done = g->done;
   h->maps_ready = (n == 0);
   h->ll_half = -1;
   h->pend = Handle::kPendNone;
@@ -587,6 +593,40 @@ EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_id
   ++g->stats.handles_created;
   trace(g, "create_handle", n);
   return EP_OK;
+}
+
+}  // namespace
+
+EP_API ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t* topk_idx, ep_stream_t stream,
+                                    ep_handle_t* out) {
+  Group* g = reinterpret_cast<Group*>(group);
+  if (!group_ok(g) || !out) return EP_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const int K = g->cfg.top_k;
+  if (!check2d(topk_idx, EP_DTYPE_I32, -1, K, EP_TAG_TOPK_IDX, false) || !contiguous2d(topk_idx))
+    return EP_ERR_INVALID_ARGUMENT;
+  return make_handle(g, static_cast<const int32_t*>(topk_idx->data), nullptr, 0, nullptr, topk_idx->sizes[0],
+                     as_stream(stream), out);
+}
+
+EP_API ep_status_t ep_route_handle(ep_group_t group, const ep_tensor_t* scores, ep_tensor_t* topk_idx,
+                                   ep_stream_t stream, ep_handle_t* out) {
+  Group* g = reinterpret_cast<Group*>(group);
+  if (!group_ok(g) || !out) return EP_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  const int E = g->cfg.num_experts, K = g->cfg.top_k;
+  if (!check2d(scores, EP_DTYPE_F32, -1, E, EP_TAG_TOKENS, false)) return EP_ERR_INVALID_ARGUMENT;
+  const int64_t n = scores->sizes[0];
+  if (!check2d(topk_idx, EP_DTYPE_I32, n, K, EP_TAG_TOPK_IDX, false) || !contiguous2d(topk_idx))
+    return EP_ERR_INVALID_ARGUMENT;
+  const ep_status_t st = make_handle(g, nullptr, static_cast<const float*>(scores->data), scores->strides[0],
+                                     static_cast<int32_t*>(topk_idx->data), n, as_stream(stream), out);
+  if (st == EP_OK) {
+    ++g->stats.route_calls;
+    g->stats.tokens_routed += n;
+    trace(g, "route", n);
+  }
+  return st;
 }
 
 EP_API ep_status_t ep_destroy_handle(ep_handle_t handle) {

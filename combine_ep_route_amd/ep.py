@@ -155,6 +155,15 @@ def ep_create_handle(group: Group, topk_idx: torch.Tensor, stream=None) -> Handl
     return Handle(out.value, group, topk_idx.shape[0])
 
 
+def ep_route_handle(group: Group, scores: torch.Tensor, topk_idx: torch.Tensor, stream=None) -> Handle:
+    out = ctypes.c_void_p()
+    sc = desc(scores, A.EP_TAG_TOKENS)
+    t = desc(topk_idx, A.EP_TAG_TOPK_IDX)
+    _check("ep_route_handle", A.lib().ep_route_handle(group.ptr, _ref(sc), _ref(t), _stream(stream),
+                                                      ctypes.byref(out)))
+    return Handle(out.value, group, topk_idx.shape[0])
+
+
 def ep_destroy_handle(handle: Handle) -> None:
     _check("ep_destroy_handle", A.lib().ep_destroy_handle(handle.ptr))
 

@@ -230,6 +230,22 @@ ep_status_t ep_route(ep_group_t group, const ep_tensor_t *scores,
 ep_status_t ep_create_handle(ep_group_t group, const ep_tensor_t *topk_idx,
                              ep_stream_t stream, ep_handle_t *out);
 
+/* Routing and handle creation in one pass: ep_route of `scores` into
+ * topk_idx, then ep_create_handle from it, with the same results as the two
+ * calls ("NVSHMEM and DeepEP", high-throughput section: the routing decision
+ * fixes every count and position of the dispatch; "NCCL EP paper notes",
+ * core functions: the handle is built from topk_idx).  The routing and the
+ * counting share one kernel whenever the routing's fast path applies
+ * (E a multiple of 128 up to 512, a node spanning a power-of-two number of
+ * 32-lane groups, node sums of at most 2 scores, 16-byte aligned score
+ * rows); otherwise the two run back to back.
+ *   scores   : F32 [n, E], row stride >= E; n = S*T, T <= T_max.
+ *   topk_idx : I32 [n, K] out, contiguous; the caller owns it (the handle
+ *              keeps its own copy).
+ * Errors: as ep_route and ep_create_handle together. */
+ep_status_t ep_route_handle(ep_group_t group, const ep_tensor_t *scores, ep_tensor_t *topk_idx,
+                            ep_stream_t stream, ep_handle_t *out);
+
 /* Return the handle's storage to the group (NCCL-EP ncclEpHandleDestroy).
  * Stream-ordered reuse: work already enqueued with the handle may still run.
  * The value must not be used afterwards: until a new handle takes the same

@@ -79,7 +79,7 @@ def _declare(l):
     l.orc_token_row.restype = None
     l.orc_pack_ll.argtypes = [_P, _L, _I, _I, _I, _I, _P, _L, _P]
     l.orc_pack_ll.restype = None
-    l.orc_pack_ht.argtypes = [_P, _P, _P, _L, _I, _I, _I, _I, _I, _P, _P,
+    l.orc_pack_ht.argtypes = [_P, _P, _P, _L, _L, _I, _I, _I, _I, _I, _P, _P,
                               _P, _P, _P, _P, _P, _P, _P, _P, _P]
     l.orc_pack_ht.restype = None
     l.orc_dequant_rows.argtypes = [_P, _L, _L, _I, _I, _P]
@@ -233,24 +233,30 @@ def pack_ll(x_bits: np.ndarray, tokens_per_src: int, top_k: int, fp8: bool,
 
 
 def pack_ht(x_bits, topk, weights, tokens_per_src, num_nodes, fp8, node_row, row2,
-            rows1, rows2, with_payload=True):
+            rows1, rows2, with_payload=True, out=None, first_token=0):
     """HT stage-1/stage-2 rows and metadata.  With with_payload=False only the
-    metadata is produced and x_bits may be any [*, H] array (unused)."""
+    metadata is produced and x_bits may be any [*, H] array (unused).
+
+    With `out` (a dict as returned by a previous call) the rows of the given
+    tokens are written into it, the tokens being tokens first_token ... of
+    the batch (x_bits, topk, weights, node_row and row2 hold just those), so
+    that disjoint token ranges can be packed into one set of rows."""
     x = _c(x_bits, np.uint16)
     H = x.shape[1]
     n, K = topk.shape
     if with_payload and x.shape[0] != n:
         raise ValueError("x must hold every token when payload rows are produced")
     rb = row_bytes(H, fp8)
-    out = dict(
-        stage1=np.zeros((rows1, rb), np.uint8) if with_payload else None,
-        meta1_tok=np.zeros(rows1, np.int32), meta1_src=np.zeros(rows1, np.int32),
-        meta1_topk=np.zeros((rows1, K), np.int32), meta1_w=np.zeros((rows1, K), np.float32),
-        stage2=np.zeros((rows2, rb), np.uint8) if with_payload else None,
-        meta2_src=np.zeros(rows2, np.int32), meta2_tok=np.zeros(rows2, np.int32),
-        meta2_k=np.zeros(rows2, np.int32))
+    if out is None:
+        out = dict(
+            stage1=np.zeros((rows1, rb), np.uint8) if with_payload else None,
+            meta1_tok=np.zeros(rows1, np.int32), meta1_src=np.zeros(rows1, np.int32),
+            meta1_topk=np.zeros((rows1, K), np.int32), meta1_w=np.zeros((rows1, K), np.float32),
+            stage2=np.zeros((rows2, rb), np.uint8) if with_payload else None,
+            meta2_src=np.zeros(rows2, np.int32), meta2_tok=np.zeros(rows2, np.int32),
+            meta2_k=np.zeros(rows2, np.int32))
     w = None if weights is None else _c(weights, np.float32)
-    lib().orc_pack_ht(_ptr(x), _ptr(_c(topk, np.int32)), _ptr(w), n, tokens_per_src,
+    lib().orc_pack_ht(_ptr(x), _ptr(_c(topk, np.int32)), _ptr(w), first_token, n, tokens_per_src,
                       H, K, num_nodes, int(fp8), _ptr(_c(node_row, np.int32)),
                       _ptr(_c(row2, np.int32)), _ptr(out["stage1"]), _ptr(out["meta1_tok"]),
                       _ptr(out["meta1_src"]), _ptr(out["meta1_topk"]), _ptr(out["meta1_w"]),

@@ -486,9 +486,12 @@ void orc_pack_ll(const uint16_t *x, int64_t n_tok, int T, int H, int K, int fp8,
  *   stage 1: meta1_tok[row]=t, meta1_src[row]=s, meta1_topk[row*K..]=topk_idx
  *            of the token, meta1_w[row*K..]=topk_weights (if w != NULL)
  *   stage 2: meta2_src[row]=s, meta2_tok[row]=t, meta2_k[row]=k
+ * The n_tok tokens given are tokens i0 .. i0+n_tok-1 of the batch (token
+ * i = s*T + t); x, topk, w, node_row and row2 start at token i0, the row
+ * arrays are the whole batch's.
  * With both stage pointers NULL only the metadata is produced (x unused). */
 void orc_pack_ht(const uint16_t *x, const int32_t *topk, const float *w,
-                 int64_t n_tok, int T, int H, int K, int N, int fp8,
+                 int64_t i0, int64_t n_tok, int T, int H, int K, int N, int fp8,
                  const int32_t *node_row, const int32_t *row2,
                  uint8_t *stage1, int32_t *meta1_tok, int32_t *meta1_src,
                  int32_t *meta1_topk, float *meta1_w,
@@ -498,7 +501,7 @@ void orc_pack_ht(const uint16_t *x, const int32_t *topk, const float *w,
     const int64_t row_bytes = fp8 ? (int64_t)H + (H / 128) * 4 : (int64_t)H * 2;
     uint8_t *img = malloc((size_t)row_bytes);
     for (int64_t i = 0; i < n_tok; ++i) {
-        const int32_t t = (int32_t)(i % T), s = (int32_t)(i / T);
+        const int32_t t = (int32_t)((i0 + i) % T), s = (int32_t)((i0 + i) / T);
         if (stage1 || stage2) orc_token_row(x + i * H, H, fp8, img);
         for (int n = 0; n < N; ++n) {
             int32_t r = node_row[i * N + n];

@@ -25,7 +25,7 @@ void orc_quantize_row(const uint16_t *x, int H, uint8_t *q, float *scales);
 void orc_token_row(const uint16_t *x, int H, int fp8, uint8_t *dst);
 void orc_pack_ll(const uint16_t *x, int64_t n_tok, int T, int H, int K, int fp8, const int32_t *slot_map,
                  int64_t msg_bytes, uint8_t *buf);
-void orc_pack_ht(const uint16_t *x, const int32_t *topk, const float *w, int64_t n_tok, int T, int H, int K,
+void orc_pack_ht(const uint16_t *x, const int32_t *topk, const float *w, int64_t i0, int64_t n_tok, int T, int H, int K,
                  int N, int fp8, const int32_t *node_row, const int32_t *row2, uint8_t *stage1,
                  int32_t *meta1_tok, int32_t *meta1_src, int32_t *meta1_topk, float *meta1_w, uint8_t *stage2,
                  int32_t *meta2_src, int32_t *meta2_tok, int32_t *meta2_k);
@@ -100,7 +100,7 @@ int main(void) {
     float *m1w = xalloc(sizeof(float) * rows1 * K);
     int32_t *m2s = xalloc(sizeof(int32_t) * rows2), *m2t = xalloc(sizeof(int32_t) * rows2);
     int32_t *m2k = xalloc(sizeof(int32_t) * rows2);
-    orc_pack_ht(x, topk, w, NT, T, H, K, N, 1, node_row, row2, st1, m1t, m1s, m1k, m1w, st2, m2s, m2t, m2k);
+    orc_pack_ht(x, topk, w, 0, NT, T, H, K, N, 1, node_row, row2, st1, m1t, m1s, m1k, m1w, st2, m2s, m2t, m2k);
 
     /* per-rank stage 2 */
     int32_t *rc2 = xalloc(sizeof(int32_t) * R), *roff2 = xalloc(sizeof(int32_t) * R);

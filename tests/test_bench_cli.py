@@ -5,6 +5,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -71,12 +72,45 @@ def test_cpu_baseline_object(monkeypatch):
     scores = I.page_scores(n, 256, 0)
     w = I.normal_weights(n, 8, 0)
     cb = bench.cpu_baseline(scores, I.normal_bf16(n, 7168, 1), w, I.normal_bf16(n * 8, 7168, 2), n)
-    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["cores"] == 1 and cb["runs"] == 1
+    assert cb["kind"] == "oracle" and cb["unit"] == "GB/s" and cb["runs"] == 1
+    assert cb["cores"] == bench.host_threads() and cb["nproc"] == os.cpu_count()
     assert cb["value"] > 0 and f"{n} tokens" in cb["sample"]
+    st = cb["single_thread"]
+    assert st["cores"] == 1 and st["runs"] == 1 and st["value"] > 0
     lay = oracle.layout_ht(oracle.route(scores, 8, 8, 4), 1, 256, 8, 8)
     ab = bench.algorithmic_bytes(n, 8, 7168, int(lay["c1"].sum()), int(lay["c2"].sum()), 256)["total"]
     # seconds is rounded to the millisecond
-    assert abs(cb["value"] - ab / cb["seconds"] / 1e9) <= cb["value"] * (0.01 + 0.0006 / cb["seconds"])
+    for leg in (cb, st):
+        assert abs(leg["value"] - ab / leg["seconds"] / 1e9) <= leg["value"] * (0.01 + 0.0006 / leg["seconds"])
+
+
+def test_oracle_on_token_ranges_equals_the_whole_batch():
+    """The multi-core CPU baseline runs the oracle's per-token stages on
+    disjoint token ranges: routing, packing (rows written into one set) and
+    the combine over ranges give exactly the whole batch's results."""
+    import ep_inputs as I
+    import oracle
+    n, H = 300, 256
+    scores = I.page_scores(n, 256, 3).astype(np.float32)
+    xb = I.bf16_bits(I.normal_bf16(n, H, 4))
+    w = I.normal_weights(n, 8, 5)
+    parts = [(0, 77), (77, 78), (78, 300)]
+    topk = oracle.route(scores, 8, 8, 4)
+    topk_p = np.concatenate([oracle.route(scores[a:b], 8, 8, 4) for a, b in parts])
+    np.testing.assert_array_equal(topk_p, topk)
+    lay = oracle.layout_ht(topk, 1, 256, 8, 8)
+    r1, r2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+    whole = oracle.pack_ht(xb, topk, w, n, 8, True, lay["node_row"], lay["row2"], r1, r2)
+    pk = oracle.pack_ht(xb[:0], topk[:0], w[:0], n, 8, True, lay["node_row"][:0], lay["row2"][:0], r1, r2)
+    for a, b in parts:
+        oracle.pack_ht(xb[a:b], topk[a:b], w[a:b], n, 8, True, lay["node_row"][a:b], lay["row2"][a:b],
+                       r1, r2, out=pk, first_token=a)
+    for k in whole:
+        np.testing.assert_array_equal(pk[k], whole[k], err_msg=k)
+    y = oracle.dequant_rows(whole["stage2"], H, True)
+    out = oracle.combine(y, w, lay["row2"])
+    out_p = np.concatenate([oracle.combine(y, w, lay["row2"], which=np.arange(a, b)) for a, b in parts])
+    np.testing.assert_array_equal(out_p, out)
 
 
 def test_stored_round_trip_traffic_is_consistent():

@@ -17,9 +17,9 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 def test_bench_json_line():
     need_gpu()
-    say("bench.py --steps 8 --warmup 2 --no-cpu-baseline")
+    say("bench.py --steps 8 --warmup 2 --no-cpu-baseline --no-secondary")
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "8", "--warmup", "2",
-                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=100,
+                        "--no-cpu-baseline", "--no-secondary"], capture_output=True, text=True, timeout=100,
                        env=dict(os.environ, WORLD_SIZE="1"))
     assert r.returncode == 0, r.stderr[-2000:]
     lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
@@ -40,4 +40,28 @@ def test_bench_json_line():
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
     assert rf["traffic"] is None or abs(rf["traffic"] / rf["algorithmic_bytes_per_launch"] - 1) < 0.05
     assert 0 < d["value"] < 8000.0 and 0 < rf["achieved"] < 8000.0
-    assert "cpu_baseline" not in d
+    assert "cpu_baseline" not in d and "secondary" not in d
+    assert set(d["kernel_ms"]) == {"route_handle", "dispatch", "combine"}
+
+
+def test_bench_secondary_lines():
+    """The default run adds the 64 x 128 LL decode and the 16384-token round
+    trip, each with its own step time, GB/s and roofline kernel."""
+    need_gpu()
+    say("bench.py --steps 4 --warmup 1 --no-cpu-baseline (with the secondary workloads)")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--steps", "4", "--warmup", "1",
+                        "--no-cpu-baseline"], capture_output=True, text=True, timeout=110,
+                       env=dict(os.environ, WORLD_SIZE="1"))
+    assert r.returncode == 0, r.stderr[-2000:]
+    lines = [l for l in r.stdout.splitlines() if l.startswith("{")]
+    assert len(lines) == 1
+    d = json.loads(lines[0])
+    assert d["config"]["workload"] == "ht_prefill_4096_plus_combine"
+    sec = d["secondary"]
+    assert sec["ll_decode_64x128"]["workload"] == "ll_decode_64x128_plus_combine"
+    assert sec["round_trip_16384_zipf"]["workload"] == "ht_round_trip_16384_zipf_plus_combine"
+    for line in sec.values():
+        assert abs(line["gbs"] - line["algorithmic_bytes_per_step"] / (line["ms_per_step"] * 1e-3) / 1e9) \
+            <= 0.01 * line["gbs"]
+        assert line["roofline"]["kernel"] in ("dispatch", "combine")
+        assert 0 < line["gbs"] < 8000.0
