@@ -69,6 +69,7 @@ struct Group {
   uint8_t* ll_buf[2] = {nullptr, nullptr};   // LL receive buffers, used in turn
   int ll_nbuf = 0;
   int ll_next = 0;                           // buffer the next LL dispatch takes
+  uint64_t buf_gen[2] = {0, 0};              // dispatches into each receive buffer (HT: [0], the stage rows)
   uint8_t* st1 = nullptr;
   int32_t* m1_tok = nullptr;
   int32_t* m1_src = nullptr;
@@ -122,6 +123,8 @@ struct Handle {
   int32_t* hist_e = nullptr;     // [tiles_max, E] tile counts -> prefixes
   int32_t* hist_n = nullptr;     // [tiles_max, N]
   int ll_half = -1;              // LL receive buffer of the last dispatch
+  bool dispatched = false;       // a dispatch has written this handle's rows
+  uint64_t buf_gen = 0;          // the buffer's dispatch count when this handle wrote it
 
   // Staged (send_only) operation awaiting ep_complete: at most one.
   enum { kPendNone = 0, kPendDispatch = 1, kPendCombine = 2 };

@@ -575,6 +575,7 @@ ep_status_t make_handle(Group* g, const int32_t* topk, const float* scores, int6
   a.done = g->done;
   h->maps_ready = (n == 0);
   h->ll_half = -1;
+  h->dispatched = false;
   h->pend = Handle::kPendNone;
   if (n == 0 && a.ht) {
     // Nothing routed: counts and offsets are zero.
@@ -773,6 +774,11 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
     h->ll_half = half;
     g->ll_next = (half + 1) % g->ll_nbuf;
   }
+  // Every dispatch into a receive buffer overwrites the rows an earlier
+  // handle left there: the buffer's count tells a handle whether its rows
+  // are still in place.
+  h->dispatched = true;
+  h->buf_gen = ++g->buf_gen[ll ? half : 0];
   if (send_only) {
     // The receive stage waits for ep_complete.
     h->pend = Handle::kPendDispatch;
@@ -845,11 +851,20 @@ EP_API ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t* v
   return buffer_view(g, which, 0, view);
 }
 
+namespace {
+// A dispatched handle whose receive rows a later dispatch has overwritten.
+bool rows_overwritten(const Handle* h) {
+  const bool ll = h->g->cfg.mode == EP_MODE_LL;
+  return h->dispatched && h->buf_gen != h->g->buf_gen[ll ? h->ll_half : 0];
+}
+}  // namespace
+
 EP_API ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t* view) {
   Handle* h = reinterpret_cast<Handle*>(handle);
   if (!handle_ok(h) || !view) return EP_ERR_INVALID_ARGUMENT;
   const bool ll = h->g->cfg.mode == EP_MODE_LL;
   if (ll && which == EP_BUF_LL_RECV && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;
+  if (rows_overwritten(h)) return EP_ERR_INVALID_ARGUMENT;
   return buffer_view(h->g, which, ll ? h->ll_half : 0, view);
 }
 
@@ -860,6 +875,7 @@ EP_API ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t wh
   if (rank < 0 || rank >= g->R) return EP_ERR_INVALID_ARGUMENT;
   const bool ll = g->cfg.mode == EP_MODE_LL;
   if (ll && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;   // not dispatched: no buffer yet
+  if (rows_overwritten(h)) return EP_ERR_INVALID_ARGUMENT;
   ep_tensor_t full;
   if (const ep_status_t st = buffer_view(g, which, ll ? h->ll_half : 0, &full); st != EP_OK) return st;
   int64_t first = 0, count = 0;

@@ -380,7 +380,11 @@ ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
 
 /* As ep_get_buffer, but EP_BUF_LL_RECV is the receive buffer the handle's
  * last dispatch wrote (ep_get_buffer returns the first of the group's LL
- * buffers).  EP_ERR_INVALID_ARGUMENT for an LL handle not yet dispatched. */
+ * buffers).  EP_ERR_INVALID_ARGUMENT for an LL handle not yet dispatched,
+ * and for a handle whose rows a later dispatch on the group has overwritten:
+ * in LL the next dispatch (of any handle) that takes the same receive
+ * buffer -- the group's ll_buffers buffers are taken in turn --, in HT any
+ * later dispatch.  The handle's maps, counts and combine stay valid. */
 ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t *view);
 
 /* One destination rank's partition of a receive buffer: the view of
@@ -399,8 +403,9 @@ ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t 
  * so the HT forms synchronise the handle's stream and read two counters, as
  * ep_handle_get_num_recv does; the LL form does not block.  The rows hold
  * data once the handle's dispatch has run.  EP_ERR_INVALID_ARGUMENT for a
- * rank outside [0, R), a buffer id of the other mode, or an LL handle not
- * yet dispatched. */
+ * rank outside [0, R), a buffer id of the other mode, an LL handle not yet
+ * dispatched, or a handle whose rows a later dispatch has overwritten (as
+ * for ep_handle_get_buffer). */
 ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t which, ep_tensor_t *view);
 
 /* ----------------------------------------------------------------------- */

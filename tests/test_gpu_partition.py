@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import A, I, buffer, dev, ep, host, need_gpu, say
+from gpu_util import A, I, buffer, dev, ep, get_map, host, need_gpu, say
 
 pytestmark = pytest.mark.gpu
 
@@ -152,8 +152,54 @@ def test_ll_partitions_follow_the_handles_buffer():
         ep.ep_dispatch(h2, x.cuda())
         assert ep.ep_get_partition(h2, 1, A.EP_BUF_LL_RECV).data_ptr() != \
             ep.ep_get_partition(h, 1, A.EP_BUF_LL_RECV).data_ptr()
+        # a third dispatch takes the first buffer again: the first handle's
+        # messages are gone, so its views are refused; the others stay
+        h3 = ep.ep_create_handle(g, dev(topk))
+        ep.ep_dispatch(h3, x.cuda())
+        for fn in (lambda: ep.ep_get_partition(h, 1, A.EP_BUF_LL_RECV),
+                   lambda: ep.ep_handle_get_buffer(h, A.EP_BUF_LL_RECV)):
+            with pytest.raises(ep.EpError):
+                fn()
+        assert ep.ep_get_partition(h3, 1, A.EP_BUF_LL_RECV).data_ptr() == full[per].data_ptr()
+        assert ep.ep_get_partition(h2, 1, A.EP_BUF_LL_RECV).data_ptr() != full[per].data_ptr()
         torch.cuda.synchronize()
+        ep.ep_destroy_handle(h3)
         ep.ep_destroy_handle(h2)
         ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
+def test_ht_views_of_an_overwritten_handle_are_refused():
+    """HT keeps one set of stage rows: after a second handle's dispatch the
+    first handle's partitions and buffer views are refused, its maps and
+    counts stay, and the second handle's views are served."""
+    w = I.HT_PREFILL.with_(tokens_per_rank=200, hidden=256, seed=61)
+    g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=256, top_k=8,
+                           max_nodes_per_token=4, hidden=256, max_tokens_per_rank=200, num_src_ranks=1,
+                           payload="fp8", max_handles=2)
+    try:
+        hs, topks = [], []
+        for j in range(2):
+            tk = torch.empty((200, 8), dtype=torch.int32, device="cuda")
+            hs.append(ep.ep_route_handle(g, dev(I.scores_for(w.with_(seed=61 + j))), tk))
+            topks.append(host(tk))
+        x = I.normal_bf16(200, 256, 62).cuda()
+        ep.ep_dispatch(hs[0], x)
+        p0 = host(ep.ep_get_partition(hs[0], 3, A.EP_BUF_HT_STAGE1_TOKEN))
+        ep.ep_dispatch(hs[1], x)
+        for which in (A.EP_BUF_HT_STAGE1, A.EP_BUF_HT_STAGE2, A.EP_BUF_HT_STAGE2_SRC):
+            with pytest.raises(ep.EpError):
+                ep.ep_get_partition(hs[0], 3, which)
+            with pytest.raises(ep.EpError):
+                ep.ep_handle_get_buffer(hs[0], which)
+        lay0 = oracle.layout_ht(topks[0], 1, 256, 8, 8)
+        np.testing.assert_array_equal(get_map(hs[0], A.EP_MAP_HT_ROW), lay0["row2"])
+        lay1 = oracle.layout_ht(topks[1], 1, 256, 8, 8)
+        c = int(lay1["c1"][3])
+        got = host(ep.ep_get_partition(hs[1], 3, A.EP_BUF_HT_STAGE1_TOKEN))
+        assert len(got) == c and len(p0) == int(lay0["c1"][3])
+        for h in hs:
+            ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
