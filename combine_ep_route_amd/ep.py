@@ -54,9 +54,12 @@ def desc(t: Optional[torch.Tensor], tag: int = A.EP_TAG_NONE):
     d.data = t.data_ptr()
     d.dtype = _DTYPES[t.dtype]
     d.ndim = t.dim()
+    # an empty tensor may report any strides (numpy's give 0s): describe it
+    # as the contiguous tensor it trivially is
+    strides = t.stride() if t.numel() > 0 else torch.empty(t.shape, device="meta").stride()
     for i in range(t.dim()):
         d.sizes[i] = t.shape[i]
-        d.strides[i] = t.stride(i)
+        d.strides[i] = strides[i]
     d.tag = tag
     return d
 
@@ -162,6 +165,20 @@ def ep_route_handle(group: Group, scores: torch.Tensor, topk_idx: torch.Tensor, 
     _check("ep_route_handle", A.lib().ep_route_handle(group.ptr, _ref(sc), _ref(t), _stream(stream),
                                                       ctypes.byref(out)))
     return Handle(out.value, group, topk_idx.shape[0])
+
+
+def ep_layout_noalloc(topk_idx: torch.Tensor, maps: dict, device_error: Optional[torch.Tensor] = None,
+                      stream=None, **config) -> None:
+    """The handle's maps for topk_idx without a group or an allocation:
+    maps is {ep_map_t id: int32 device tensor} for the configuration's mode;
+    config takes ep_create_group's keyword arguments."""
+    cfg = make_config(**config)
+    t = desc(topk_idx, A.EP_TAG_TOPK_IDX)
+    descs = [desc(maps[m]) if m in maps else None for m in range(8)]
+    arr = (ctypes.POINTER(A.EpTensor) * 8)(*[ctypes.pointer(d) if d is not None else None for d in descs])
+    err = desc(device_error)
+    _check("ep_layout_noalloc", A.lib().ep_layout_noalloc(ctypes.byref(cfg), _ref(t), arr, _ref(err),
+                                                          _stream(stream)))
 
 
 def ep_destroy_handle(handle: Handle) -> None:
