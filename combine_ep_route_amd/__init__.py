@@ -9,7 +9,7 @@ and the weighted top-k combine.  This package is its thin Python binding.
 from . import _abi  # noqa: F401
 from .ep import (  # noqa: F401
     EpError, Group, Handle, desc, ep_combine, ep_combine_backward, ep_complete, ep_create_group,
-    ep_create_handle, ep_dispatch_backward,
+    ep_create_handle, ep_dispatch_backward, ep_layout_noalloc,
     ep_dequantize_rows, ep_destroy_group, ep_destroy_handle, ep_dispatch,
     ep_get_buffer, ep_get_device_error, ep_get_partition, ep_group_stats, ep_handle_get_buffer, ep_handle_get_map,
     ep_handle_get_num_recv, ep_last_hip_error, ep_quantize, ep_route, ep_route_handle, ep_status_string,

@@ -53,6 +53,8 @@ EP_MAP_HT_RANK_OFFSET = 5
 EP_MAP_HT_EXPERT_COUNT = 6
 EP_MAP_HT_EXPERT_OFFSET = 7
 
+EP_NOALLOC_SCRATCH_BYTES = 8 * 1024 * 1024
+
 EP_BUF_LL_RECV = 0
 EP_BUF_HT_STAGE1 = 1
 EP_BUF_HT_STAGE1_TOKEN = 2
@@ -127,6 +129,7 @@ SIGNATURES = {
     "ep_create_handle": (_S, [_P, _PT, _P, ctypes.POINTER(_P)]),
     "ep_route_handle": (_S, [_P, _PT, _PT, _P, ctypes.POINTER(_P)]),
     "ep_destroy_handle": (_S, [_P]),
+    "ep_layout_noalloc": (_S, [ctypes.POINTER(EpConfig), _PT, ctypes.POINTER(_PT), _PT, _P]),
     "ep_handle_get_num_recv": (_S, [_P, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64)]),
     "ep_handle_get_map": (_S, [_P, ctypes.c_int32, _PT]),
     "ep_dispatch": (_S, [_P, _PT, _PT, _PT, _PT, ctypes.c_int32, _P]),

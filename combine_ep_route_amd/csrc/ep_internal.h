@@ -42,6 +42,22 @@ struct CombineArgs {
 
 struct Handle;
 
+// log2(v) if v is a power of two, else -1.
+inline int log2_exact(int v) {
+  if (v <= 0 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) < v) ++s;
+  return s;
+}
+
+// Routing topology derived from a configuration, checked: shared by group
+// creation and the group-free layout.  Checks mode, topology, K, M, T_max,
+// S and the stage-2 kind (not the payload, hidden size or buffers).
+struct Topology {
+  int R, L, P, M, J, E2, s2_rank;
+};
+ep_status_t check_topology(const ep_config_t& cfg, Topology* t);
+
 struct Group {
   uint32_t magic = kGroupMagic;
   ep_config_t cfg{};

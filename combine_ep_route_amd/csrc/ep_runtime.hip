@@ -169,14 +169,6 @@ int dispatch_block_cap(const Group* g) {
   return g->cfg.num_cus > 0 ? g->cfg.num_cus * 4 : 0;
 }
 
-// log2(v) if v is a power of two, else -1.
-int log2_exact(int v) {
-  if (v <= 0 || (v & (v - 1)) != 0) return -1;
-  int s = 0;
-  while ((1 << s) < v) ++s;
-  return s;
-}
-
 // The handle-dependent part of a dispatch launch.
 DispatchArgs dispatch_base(const Handle* h) {
   const Group* g = h->g;
@@ -277,23 +269,17 @@ using namespace ep;
 // Groups
 // ===========================================================================
 
-EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream, ep_group_t* out) {
-  if (!cfg_in || !out) return EP_ERR_INVALID_ARGUMENT;
-  *out = nullptr;
-  ep_config_t cfg = *cfg_in;
+namespace ep {
+
+ep_status_t check_topology(const ep_config_t& cfg, Topology* t) {
   if (cfg.mode != EP_MODE_LL && cfg.mode != EP_MODE_HT) return EP_ERR_INVALID_ARGUMENT;
   if (cfg.num_nodes <= 0 || cfg.ranks_per_node <= 0 || cfg.num_experts <= 0 || cfg.top_k <= 0 ||
-      cfg.hidden <= 0 || cfg.max_tokens_per_rank <= 0 || cfg.num_src_ranks <= 0 ||
-      cfg.max_nodes_per_token < 0 || cfg.max_handles < 0 || cfg.num_cus < 0 || cfg.ll_buffers < 0 ||
-      cfg.ll_buffers > 2 || (cfg.ht_stage2 != EP_HT_STAGE2_PER_EXPERT && cfg.ht_stage2 != EP_HT_STAGE2_PER_RANK))
+      cfg.max_tokens_per_rank <= 0 || cfg.num_src_ranks <= 0 || cfg.max_nodes_per_token < 0 ||
+      (cfg.ht_stage2 != EP_HT_STAGE2_PER_EXPERT && cfg.ht_stage2 != EP_HT_STAGE2_PER_RANK))
     return EP_ERR_INVALID_ARGUMENT;
   const int64_t R = static_cast<int64_t>(cfg.num_nodes) * cfg.ranks_per_node;
   if (cfg.num_experts % R != 0) return EP_ERR_INVALID_ARGUMENT;
   if (cfg.top_k > cfg.num_experts) return EP_ERR_INVALID_ARGUMENT;
-  if (cfg.payload != EP_DTYPE_FP8_E4M3 && cfg.payload != EP_DTYPE_BF16) return EP_ERR_INVALID_ARGUMENT;
-  if (cfg.payload == EP_DTYPE_FP8_E4M3 && cfg.hidden % 128 != 0) return EP_ERR_INVALID_ARGUMENT;
-  if (cfg.hidden % 16 != 0) return EP_ERR_INVALID_ARGUMENT;
-  if ((cfg.alloc_fn == nullptr) != (cfg.free_fn == nullptr)) return EP_ERR_INVALID_ARGUMENT;
   const int N = cfg.num_nodes, K = cfg.top_k, E = cfg.num_experts;
   const int P = E / N;
   int M = cfg.max_nodes_per_token;
@@ -301,10 +287,37 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   const int J = M > 0 ? (K + M - 1) / M : 0;
   if (M > 0 && (J > P || static_cast<int64_t>(M) * P < K)) return EP_ERR_INVALID_ARGUMENT;
   if (cfg.num_src_ranks > R) return EP_ERR_UNSUPPORTED;
-  if (E > kMaxExperts || K > kMaxTopK || N > kMaxNodes || R > kMaxRanks || cfg.hidden > kMaxHidden)
-    return EP_ERR_UNSUPPORTED;
-  const bool s2_rank = cfg.mode == EP_MODE_HT && cfg.ht_stage2 == EP_HT_STAGE2_PER_RANK;
-  const int E2 = s2_rank ? static_cast<int>(R) : E;
+  if (E > kMaxExperts || K > kMaxTopK || N > kMaxNodes || R > kMaxRanks) return EP_ERR_UNSUPPORTED;
+  t->R = static_cast<int>(R);
+  t->L = E / t->R;
+  t->P = P;
+  t->M = M;
+  t->J = J;
+  t->s2_rank = cfg.mode == EP_MODE_HT && cfg.ht_stage2 == EP_HT_STAGE2_PER_RANK;
+  t->E2 = t->s2_rank ? t->R : E;
+  return EP_OK;
+}
+
+}  // namespace ep
+
+EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream, ep_group_t* out) {
+  if (!cfg_in || !out) return EP_ERR_INVALID_ARGUMENT;
+  *out = nullptr;
+  ep_config_t cfg = *cfg_in;
+  Topology topo{};
+  if (const ep_status_t st = check_topology(cfg, &topo); st != EP_OK) return st;
+  if (cfg.hidden <= 0 || cfg.max_handles < 0 || cfg.num_cus < 0 || cfg.ll_buffers < 0 || cfg.ll_buffers > 2)
+    return EP_ERR_INVALID_ARGUMENT;
+  if (cfg.payload != EP_DTYPE_FP8_E4M3 && cfg.payload != EP_DTYPE_BF16) return EP_ERR_INVALID_ARGUMENT;
+  if (cfg.payload == EP_DTYPE_FP8_E4M3 && cfg.hidden % 128 != 0) return EP_ERR_INVALID_ARGUMENT;
+  if (cfg.hidden % 16 != 0) return EP_ERR_INVALID_ARGUMENT;
+  if ((cfg.alloc_fn == nullptr) != (cfg.free_fn == nullptr)) return EP_ERR_INVALID_ARGUMENT;
+  if (cfg.hidden > kMaxHidden) return EP_ERR_UNSUPPORTED;
+  const int N = cfg.num_nodes, K = cfg.top_k, E = cfg.num_experts;
+  const int64_t R = topo.R;
+  const int P = topo.P, M = topo.M, J = topo.J;
+  const bool s2_rank = topo.s2_rank;
+  const int E2 = topo.E2;
   if (cfg.max_handles == 0) cfg.max_handles = 2;
   if (cfg.ll_buffers == 0) cfg.ll_buffers = 2;
   if (cfg.max_handles > 64) return EP_ERR_UNSUPPORTED;

@@ -276,6 +276,41 @@ typedef enum {
 } ep_map_t;
 ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *view);
 
+/* The handle's maps and counts without a group and without allocating:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  It
+ * computes what ep_create_handle followed by ep_handle_get_map gives for
+ * `topk_idx` under `config`, bit for bit, and writes it to the caller's
+ * buffers.
+ *   config   : the topology, K, M, T_max, S, mode and HT stage-2 kind, as
+ *              for ep_create_group (hidden, payload, handles, buffers, CU
+ *              cap and allocator hooks are not used).
+ *   topk_idx : I32 [n, K] contiguous, n = S*T with T <= T_max.
+ *   maps     : eight pointers indexed by ep_map_t.  LL: maps[EP_MAP_LL_SLOT]
+ *              (I32 [n, K]) and maps[EP_MAP_LL_COUNT] (I32 [E, S]).  HT:
+ *              maps[EP_MAP_HT_NODE_ROW] (I32 [n, N]), maps[EP_MAP_HT_ROW]
+ *              (I32 [n, K]) and the counts / offsets [R], [R], [E2], [E2]
+ *              (E2 = E, or R with the per-rank stage 2), 1-D or [., 1].
+ *              Every map of the mode is required and contiguous; the other
+ *              mode's entries must be NULL.  Device memory, caller-owned.
+ *   device_error : optional I32 [1] device buffer: set to 0, then to the
+ *              EP_DEVERR_* bits of invalid or repeated entries.
+ * Its working storage (a copy of topk_idx, in-tile ranks, tile counts, a
+ * counter) is a fixed device array of EP_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, kept until the process ends.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (other streams or
+ * threads) race and give wrong maps.  Stream-ordered and capturable (no
+ * memset or allocation is enqueued).
+ * Errors: EP_ERR_INVALID_ARGUMENT (descriptors, shapes), EP_ERR_CAPACITY
+ * (T > T_max, or more working storage than EP_NOALLOC_SCRATCH_BYTES: about
+ * 8*n*K + 4*n*N + 4*ceil(T/16)*S*(E2 + N) bytes in HT, 8*n*K +
+ * 4*ceil(T/16)*S*E in LL, i.e. up to about 51,000 tokens at K = N = 8,
+ * E = 256), EP_ERR_UNSUPPORTED (limits as for ep_create_group), EP_ERR_HIP. */
+#define EP_NOALLOC_SCRATCH_BYTES (8 * 1024 * 1024)
+ep_status_t ep_layout_noalloc(const ep_config_t *config, const ep_tensor_t *topk_idx,
+                              ep_tensor_t *const maps[8], ep_tensor_t *device_error,
+                              ep_stream_t stream);
+
 /* ----------------------------------------------------------------------- */
 /* Dispatch (A3 quantise + A4 LL pack | A5 HT stage 1 + A6 HT stage 2)       */
 /* ----------------------------------------------------------------------- */

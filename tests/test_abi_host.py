@@ -320,3 +320,50 @@ def test_stats_start_at_zero_without_hip():
     assert all(getattr(out, n) == 0 for n in A.STAT_FIELDS)
     assert A.lib().ep_group_stats(None, ctypes.byref(out)) == A.EP_ERR_INVALID_ARGUMENT
     assert A.lib().ep_destroy_group(g) == A.EP_OK
+
+
+def test_layout_noalloc_validates_before_any_hip_call():
+    """ep_layout_noalloc checks its descriptors, the batch against T_max and
+    its working storage against the fixed scratch size before touching HIP
+    (the data pointers below are never dereferenced)."""
+    lib = A.lib()
+    fake = 0x10000
+    n, K, N, R, E = 64, 8, 8, 64, 256
+    cfg = _cfg(max_tokens_per_rank=64)
+    topk = _t(fake, A.EP_DTYPE_I32, [n, K], tag=A.EP_TAG_TOPK_IDX)
+
+    def maps_ht(over=None):
+        shapes = {A.EP_MAP_HT_NODE_ROW: [n, N], A.EP_MAP_HT_ROW: [n, K], A.EP_MAP_HT_RANK_COUNT: [R],
+                  A.EP_MAP_HT_RANK_OFFSET: [R], A.EP_MAP_HT_EXPERT_COUNT: [E], A.EP_MAP_HT_EXPERT_OFFSET: [E]}
+        shapes.update(over or {})
+        ts = [None] * 8
+        for m, sh in shapes.items():
+            if sh is not None:
+                ts[m] = _t(fake, A.EP_DTYPE_I32, sh)
+        arr = (ctypes.POINTER(A.EpTensor) * 8)(*[ctypes.pointer(x) if x is not None else None for x in ts])
+        return arr, ts
+
+    def call(c, t, arr):
+        return lib.ep_layout_noalloc(ctypes.byref(c) if c is not None else None,
+                                     ctypes.byref(t) if t is not None else None, arr, None, None)
+
+    arr, keep = maps_ht()
+    assert call(None, topk, arr) == A.EP_ERR_INVALID_ARGUMENT
+    assert call(cfg, None, arr) == A.EP_ERR_INVALID_ARGUMENT
+    assert call(cfg, topk, None) == A.EP_ERR_INVALID_ARGUMENT
+    bad_dtype = _t(fake, A.EP_DTYPE_F32, [n, K])
+    assert call(cfg, bad_dtype, arr) == A.EP_ERR_INVALID_ARGUMENT
+    # more tokens per source than T_max
+    assert call(_cfg(max_tokens_per_rank=63), topk, arr) == A.EP_ERR_CAPACITY
+    # a map missing, a map of the wrong shape, an LL map given in HT
+    for over in ({A.EP_MAP_HT_ROW: None}, {A.EP_MAP_HT_NODE_ROW: [n, N + 1]}, {A.EP_MAP_HT_RANK_COUNT: [R - 1]},
+                 {A.EP_MAP_LL_SLOT: [n, K]}):
+        a2, keep2 = maps_ht(over)
+        assert call(cfg, topk, a2) == A.EP_ERR_INVALID_ARGUMENT, over
+    # an inconsistent topology
+    assert call(_cfg(num_experts=100, max_tokens_per_rank=64), topk, arr) == A.EP_ERR_INVALID_ARGUMENT
+    # working storage beyond EP_NOALLOC_SCRATCH_BYTES
+    big = 70_000
+    tb = _t(fake, A.EP_DTYPE_I32, [big, K])
+    ab, keepb = maps_ht({A.EP_MAP_HT_NODE_ROW: [big, N], A.EP_MAP_HT_ROW: [big, K]})
+    assert call(_cfg(max_tokens_per_rank=big), tb, ab) == A.EP_ERR_CAPACITY
