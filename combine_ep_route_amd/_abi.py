@@ -109,6 +109,7 @@ class EpConfig(ctypes.Structure):
         ("num_cus", ctypes.c_int32),
         ("ll_buffers", ctypes.c_int32),
         ("ht_stage2", ctypes.c_int32),
+        ("ht_buffers", ctypes.c_int32),
         ("alloc_fn", ALLOC_FN),
         ("free_fn", FREE_FN),
         ("alloc_ctx", ctypes.c_void_p),

@@ -82,21 +82,26 @@ struct Group {
   struct Alloc { void* ptr; size_t bytes; };
   std::vector<Alloc> allocs;
   int64_t bytes = 0;
-  uint8_t* ll_buf[2] = {nullptr, nullptr};   // LL receive buffers, used in turn
-  int ll_nbuf = 0;
-  int ll_next = 0;                           // buffer the next LL dispatch takes
-  uint64_t buf_gen[2] = {0, 0};              // dispatches into each receive buffer (HT: [0], the stage rows)
-  uint8_t* st1 = nullptr;
-  int32_t* m1_tok = nullptr;
-  int32_t* m1_src = nullptr;
-  int32_t* m1_topk = nullptr;
-  float* m1_w = nullptr;
-  uint8_t* st2 = nullptr;
-  int32_t* m2_src = nullptr;
-  int32_t* m2_tok = nullptr;
-  int32_t* m2_k = nullptr;
-  int32_t* m2_topk = nullptr;   // per-rank stage 2 only
-  float* m2_w = nullptr;
+  // Receive buffers, used in turn: LL fixed-slot buffers, or HT stage-row
+  // sets (stage-1 and stage-2 rows with their metadata).
+  uint8_t* ll_buf[2] = {nullptr, nullptr};
+  struct StageSet {
+    uint8_t* st1 = nullptr;
+    int32_t* m1_tok = nullptr;
+    int32_t* m1_src = nullptr;
+    int32_t* m1_topk = nullptr;
+    float* m1_w = nullptr;
+    uint8_t* st2 = nullptr;
+    int32_t* m2_src = nullptr;
+    int32_t* m2_tok = nullptr;
+    int32_t* m2_k = nullptr;
+    int32_t* m2_topk = nullptr;   // per-rank stage 2 only
+    float* m2_w = nullptr;
+  };
+  StageSet ht[2];
+  int nbuf = 0;                              // receive buffers (LL) or stage sets (HT)
+  int buf_next = 0;                          // the one the next dispatch takes
+  uint64_t buf_gen[2] = {0, 0};              // dispatches into each of them
   int32_t* err = nullptr;    // device error word
   int32_t* done = nullptr;   // HT prefix scan: its workgroups finished (0 between launches)
 
@@ -138,7 +143,7 @@ struct Handle {
   int32_t* off2 = nullptr;       // HT [E]
   int32_t* hist_e = nullptr;     // [tiles_max, E] tile counts -> prefixes
   int32_t* hist_n = nullptr;     // [tiles_max, N]
-  int ll_half = -1;              // LL receive buffer of the last dispatch
+  int buf_half = -1;             // receive buffer / stage set of the last dispatch
   bool dispatched = false;       // a dispatch has written this handle's rows
   uint64_t buf_gen = 0;          // the buffer's dispatch count when this handle wrote it
 

@@ -306,7 +306,8 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   ep_config_t cfg = *cfg_in;
   Topology topo{};
   if (const ep_status_t st = check_topology(cfg, &topo); st != EP_OK) return st;
-  if (cfg.hidden <= 0 || cfg.max_handles < 0 || cfg.num_cus < 0 || cfg.ll_buffers < 0 || cfg.ll_buffers > 2)
+  if (cfg.hidden <= 0 || cfg.max_handles < 0 || cfg.num_cus < 0 || cfg.ll_buffers < 0 || cfg.ll_buffers > 2 ||
+      cfg.ht_buffers < 0 || cfg.ht_buffers > 2)
     return EP_ERR_INVALID_ARGUMENT;
   if (cfg.payload != EP_DTYPE_FP8_E4M3 && cfg.payload != EP_DTYPE_BF16) return EP_ERR_INVALID_ARGUMENT;
   if (cfg.payload == EP_DTYPE_FP8_E4M3 && cfg.hidden % 128 != 0) return EP_ERR_INVALID_ARGUMENT;
@@ -320,6 +321,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   const int E2 = topo.E2;
   if (cfg.max_handles == 0) cfg.max_handles = 2;
   if (cfg.ll_buffers == 0) cfg.ll_buffers = 2;
+  if (cfg.ht_buffers == 0) cfg.ht_buffers = 1;
   if (cfg.max_handles > 64) return EP_ERR_UNSUPPORTED;
 
   Group* g = new (std::nothrow) Group();
@@ -357,37 +359,41 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
 
   ep_status_t st = EP_OK;
   if (cfg.mode == EP_MODE_LL) {
-    g->ll_nbuf = cfg.ll_buffers;
-    for (int b = 0; st == EP_OK && b < g->ll_nbuf; ++b)
+    g->nbuf = cfg.ll_buffers;
+    for (int b = 0; st == EP_OK && b < g->nbuf; ++b)
       g->ll_buf[b] = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(E * S * Tm * g->msg_pitch), &st));
-  } else if (st == EP_OK) {
-    g->st1 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows1_max * g->row_pitch), &st));
-    if (st == EP_OK) {
-      const size_t r1 = static_cast<size_t>(g->rows1_max);
-      const size_t bytes = align_up(r1 * 4) * 2 + align_up(r1 * K * 4) * 2;
-      uint8_t* b = static_cast<uint8_t*>(dev_alloc(g, bytes, &st));
-      if (b) {
-        Carve cv{b};
-        g->m1_tok = cv.take<int32_t>(r1);
-        g->m1_src = cv.take<int32_t>(r1);
-        g->m1_topk = cv.take<int32_t>(r1 * K);
-        g->m1_w = cv.take<float>(r1 * K);
+  } else {
+    g->nbuf = cfg.ht_buffers;
+    for (int b = 0; st == EP_OK && b < g->nbuf; ++b) {
+      Group::StageSet& hs = g->ht[b];
+      hs.st1 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows1_max * g->row_pitch), &st));
+      if (st == EP_OK) {
+        const size_t r1 = static_cast<size_t>(g->rows1_max);
+        const size_t bytes = align_up(r1 * 4) * 2 + align_up(r1 * K * 4) * 2;
+        uint8_t* b1 = static_cast<uint8_t*>(dev_alloc(g, bytes, &st));
+        if (b1) {
+          Carve cv{b1};
+          hs.m1_tok = cv.take<int32_t>(r1);
+          hs.m1_src = cv.take<int32_t>(r1);
+          hs.m1_topk = cv.take<int32_t>(r1 * K);
+          hs.m1_w = cv.take<float>(r1 * K);
+        }
       }
-    }
-    if (st == EP_OK)
-      g->st2 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows2_max * g->row_pitch), &st));
-    if (st == EP_OK) {
-      const size_t r2 = static_cast<size_t>(g->rows2_max);
-      const size_t extra = s2_rank ? align_up(r2 * K * 4) * 2 : 0;   // received top-k and weights
-      uint8_t* b = static_cast<uint8_t*>(dev_alloc(g, align_up(r2 * 4) * 3 + extra, &st));
-      if (b) {
-        Carve cv{b};
-        g->m2_src = cv.take<int32_t>(r2);
-        g->m2_tok = cv.take<int32_t>(r2);
-        g->m2_k = cv.take<int32_t>(r2);
-        if (s2_rank) {
-          g->m2_topk = cv.take<int32_t>(r2 * K);
-          g->m2_w = cv.take<float>(r2 * K);
+      if (st == EP_OK)
+        hs.st2 = static_cast<uint8_t*>(dev_alloc(g, static_cast<size_t>(g->rows2_max * g->row_pitch), &st));
+      if (st == EP_OK) {
+        const size_t r2 = static_cast<size_t>(g->rows2_max);
+        const size_t extra = s2_rank ? align_up(r2 * K * 4) * 2 : 0;   // received top-k and weights
+        uint8_t* b2 = static_cast<uint8_t*>(dev_alloc(g, align_up(r2 * 4) * 3 + extra, &st));
+        if (b2) {
+          Carve cv{b2};
+          hs.m2_src = cv.take<int32_t>(r2);
+          hs.m2_tok = cv.take<int32_t>(r2);
+          hs.m2_k = cv.take<int32_t>(r2);
+          if (s2_rank) {
+            hs.m2_topk = cv.take<int32_t>(r2 * K);
+            hs.m2_w = cv.take<float>(r2 * K);
+          }
         }
       }
     }
@@ -587,7 +593,7 @@ ep_status_t make_handle(Group* g, const int32_t* topk, const float* scores, int6
   a.err = g->err;
   a.done = g->done;
   h->maps_ready = (n == 0);
-  h->ll_half = -1;
+  h->buf_half = -1;
   h->dispatched = false;
   h->pend = Handle::kPendNone;
   if (n == 0 && a.ht) {
@@ -761,37 +767,34 @@ EP_API ep_status_t ep_dispatch(ep_handle_t handle, const ep_tensor_t* tokens, co
     p.ld_s = scales->strides[0];
   }
   p.out_fp8 = g->fp8;
-  int half = -1;
-  if (ll) {
-    half = g->ll_next;
-    p.ll_buf = g->ll_buf[half];
-  }
+  // The receive buffer (LL) or stage-row set (HT) this dispatch takes.
+  const int half = g->buf_next;
+  if (ll) p.ll_buf = g->ll_buf[half];
   p.w = topk_weights ? static_cast<const float*>(topk_weights->data) : nullptr;
-  p.st1 = g->st1;
-  p.m1_tok = g->m1_tok;
-  p.m1_src = g->m1_src;
-  p.m1_topk = g->m1_topk;
-  p.m1_w = g->m1_w;
-  p.st2 = g->st2;
-  p.m2_src = g->m2_src;
-  p.m2_tok = g->m2_tok;
-  p.m2_k = g->m2_k;
-  p.m2_topk = g->m2_topk;
-  p.m2_w = g->m2_w;
+  const Group::StageSet& hs = g->ht[ll ? 0 : half];
+  p.st1 = hs.st1;
+  p.m1_tok = hs.m1_tok;
+  p.m1_src = hs.m1_src;
+  p.m1_topk = hs.m1_topk;
+  p.m1_w = hs.m1_w;
+  p.st2 = hs.st2;
+  p.m2_src = hs.m2_src;
+  p.m2_tok = hs.m2_tok;
+  p.m2_k = hs.m2_k;
+  p.m2_topk = hs.m2_topk;
+  p.m2_w = hs.m2_w;
   if (const ep_status_t st = from_hip(launch_dispatch(p, s)); st != EP_OK) return st;
   h->maps_ready = true;
   ++g->stats.dispatch_calls;
   g->stats.tokens_dispatched += h->n;
   trace(g, send_only ? "dispatch (send stage)" : "dispatch", h->n);
-  if (ll) {
-    h->ll_half = half;
-    g->ll_next = (half + 1) % g->ll_nbuf;
-  }
+  h->buf_half = half;
+  g->buf_next = (half + 1) % g->nbuf;
   // Every dispatch into a receive buffer overwrites the rows an earlier
   // handle left there: the buffer's count tells a handle whether its rows
   // are still in place.
   h->dispatched = true;
-  h->buf_gen = ++g->buf_gen[ll ? half : 0];
+  h->buf_gen = ++g->buf_gen[half];
   if (send_only) {
     // The receive stage waits for ep_complete.
     h->pend = Handle::kPendDispatch;
@@ -834,24 +837,24 @@ EP_API ep_status_t ep_quantize(ep_group_t group, const ep_tensor_t* tokens, ep_t
 }
 
 namespace {
-ep_status_t buffer_view(Group* g, int32_t which, int ll_half, ep_tensor_t* view) {
+ep_status_t buffer_view(Group* g, int32_t which, int half, ep_tensor_t* view) {
   const bool ll = g->cfg.mode == EP_MODE_LL;
   const int K = g->cfg.top_k;
   const int64_t slots_total = static_cast<int64_t>(g->cfg.num_experts) * g->cfg.num_src_ranks *
                               g->cfg.max_tokens_per_rank;
   switch (which) {
-    case EP_BUF_LL_RECV: if (!ll) break; fill_view(view, g->ll_buf[ll_half], EP_DTYPE_U8, slots_total, g->msg_bytes, EP_TAG_TOKENS, g->msg_pitch); return EP_OK;
-    case EP_BUF_HT_STAGE1: if (ll) break; fill_view(view, g->st1, EP_DTYPE_U8, g->rows1_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
-    case EP_BUF_HT_STAGE1_TOKEN: if (ll) break; fill_view(view, g->m1_tok, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
-    case EP_BUF_HT_STAGE1_SRC: if (ll) break; fill_view(view, g->m1_src, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
-    case EP_BUF_HT_STAGE1_TOPK: if (ll) break; fill_view(view, g->m1_topk, EP_DTYPE_I32, g->rows1_max, K, EP_TAG_TOPK_IDX); return EP_OK;
-    case EP_BUF_HT_STAGE1_WEIGHTS: if (ll) break; fill_view(view, g->m1_w, EP_DTYPE_F32, g->rows1_max, K, EP_TAG_TOPK_WEIGHTS); return EP_OK;
-    case EP_BUF_HT_STAGE2: if (ll) break; fill_view(view, g->st2, EP_DTYPE_U8, g->rows2_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
-    case EP_BUF_HT_STAGE2_SRC: if (ll) break; fill_view(view, g->m2_src, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
-    case EP_BUF_HT_STAGE2_TOKEN: if (ll) break; fill_view(view, g->m2_tok, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
-    case EP_BUF_HT_STAGE2_K: if (ll) break; fill_view(view, g->m2_k, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
-    case EP_BUF_HT_STAGE2_TOPK: if (!g->s2_rank) break; fill_view(view, g->m2_topk, EP_DTYPE_I32, g->rows2_max, K, EP_TAG_TOPK_IDX); return EP_OK;
-    case EP_BUF_HT_STAGE2_WEIGHTS: if (!g->s2_rank) break; fill_view(view, g->m2_w, EP_DTYPE_F32, g->rows2_max, K, EP_TAG_TOPK_WEIGHTS); return EP_OK;
+    case EP_BUF_LL_RECV: if (!ll) break; fill_view(view, g->ll_buf[half], EP_DTYPE_U8, slots_total, g->msg_bytes, EP_TAG_TOKENS, g->msg_pitch); return EP_OK;
+    case EP_BUF_HT_STAGE1: if (ll) break; fill_view(view, g->ht[half].st1, EP_DTYPE_U8, g->rows1_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
+    case EP_BUF_HT_STAGE1_TOKEN: if (ll) break; fill_view(view, g->ht[half].m1_tok, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
+    case EP_BUF_HT_STAGE1_SRC: if (ll) break; fill_view(view, g->ht[half].m1_src, EP_DTYPE_I32, g->rows1_max, 0, EP_TAG_NONE); return EP_OK;
+    case EP_BUF_HT_STAGE1_TOPK: if (ll) break; fill_view(view, g->ht[half].m1_topk, EP_DTYPE_I32, g->rows1_max, K, EP_TAG_TOPK_IDX); return EP_OK;
+    case EP_BUF_HT_STAGE1_WEIGHTS: if (ll) break; fill_view(view, g->ht[half].m1_w, EP_DTYPE_F32, g->rows1_max, K, EP_TAG_TOPK_WEIGHTS); return EP_OK;
+    case EP_BUF_HT_STAGE2: if (ll) break; fill_view(view, g->ht[half].st2, EP_DTYPE_U8, g->rows2_max, g->row_bytes, EP_TAG_TOKENS, g->row_pitch); return EP_OK;
+    case EP_BUF_HT_STAGE2_SRC: if (ll) break; fill_view(view, g->ht[half].m2_src, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
+    case EP_BUF_HT_STAGE2_TOKEN: if (ll) break; fill_view(view, g->ht[half].m2_tok, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
+    case EP_BUF_HT_STAGE2_K: if (ll) break; fill_view(view, g->ht[half].m2_k, EP_DTYPE_I32, g->rows2_max, 0, EP_TAG_NONE); return EP_OK;
+    case EP_BUF_HT_STAGE2_TOPK: if (!g->s2_rank) break; fill_view(view, g->ht[half].m2_topk, EP_DTYPE_I32, g->rows2_max, K, EP_TAG_TOPK_IDX); return EP_OK;
+    case EP_BUF_HT_STAGE2_WEIGHTS: if (!g->s2_rank) break; fill_view(view, g->ht[half].m2_w, EP_DTYPE_F32, g->rows2_max, K, EP_TAG_TOPK_WEIGHTS); return EP_OK;
     default: break;
   }
   return EP_ERR_INVALID_ARGUMENT;
@@ -867,8 +870,7 @@ EP_API ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t* v
 namespace {
 // A dispatched handle whose receive rows a later dispatch has overwritten.
 bool rows_overwritten(const Handle* h) {
-  const bool ll = h->g->cfg.mode == EP_MODE_LL;
-  return h->dispatched && h->buf_gen != h->g->buf_gen[ll ? h->ll_half : 0];
+  return h->dispatched && h->buf_gen != h->g->buf_gen[h->buf_half];
 }
 }  // namespace
 
@@ -876,9 +878,9 @@ EP_API ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_te
   Handle* h = reinterpret_cast<Handle*>(handle);
   if (!handle_ok(h) || !view) return EP_ERR_INVALID_ARGUMENT;
   const bool ll = h->g->cfg.mode == EP_MODE_LL;
-  if (ll && which == EP_BUF_LL_RECV && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;
+  if (ll && which == EP_BUF_LL_RECV && h->buf_half < 0) return EP_ERR_INVALID_ARGUMENT;
   if (rows_overwritten(h)) return EP_ERR_INVALID_ARGUMENT;
-  return buffer_view(h->g, which, ll ? h->ll_half : 0, view);
+  return buffer_view(h->g, which, h->buf_half < 0 ? 0 : h->buf_half, view);
 }
 
 EP_API ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t which, ep_tensor_t* view) {
@@ -887,10 +889,11 @@ EP_API ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t wh
   Group* g = h->g;
   if (rank < 0 || rank >= g->R) return EP_ERR_INVALID_ARGUMENT;
   const bool ll = g->cfg.mode == EP_MODE_LL;
-  if (ll && h->ll_half < 0) return EP_ERR_INVALID_ARGUMENT;   // not dispatched: no buffer yet
+  if (ll && h->buf_half < 0) return EP_ERR_INVALID_ARGUMENT;   // not dispatched: no buffer yet
   if (rows_overwritten(h)) return EP_ERR_INVALID_ARGUMENT;
   ep_tensor_t full;
-  if (const ep_status_t st = buffer_view(g, which, ll ? h->ll_half : 0, &full); st != EP_OK) return st;
+  if (const ep_status_t st = buffer_view(g, which, h->buf_half < 0 ? 0 : h->buf_half, &full); st != EP_OK)
+    return st;
   int64_t first = 0, count = 0;
   if (ll) {
     // Rank r's experts [r*L, (r+1)*L) are one contiguous [L][S][T_max] block of slots.

@@ -105,7 +105,7 @@ class Handle:
 def make_config(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=256, top_k=8,
                 max_nodes_per_token=4, hidden=7168, max_tokens_per_rank=128,
                 num_src_ranks=1, payload="fp8", max_handles=0, num_cus=0, ll_buffers=0, ht_stage2="expert",
-                alloc_fn=None, free_fn=None, alloc_ctx=None) -> A.EpConfig:
+                ht_buffers=0, alloc_fn=None, free_fn=None, alloc_ctx=None) -> A.EpConfig:
     c = A.EpConfig()
     c.mode = {"ll": A.EP_MODE_LL, "ht": A.EP_MODE_HT}[mode] if isinstance(mode, str) else mode
     c.num_nodes = num_nodes
@@ -123,6 +123,7 @@ def make_config(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=256, top_k
     c.ll_buffers = ll_buffers
     c.ht_stage2 = {"expert": A.EP_HT_STAGE2_PER_EXPERT, "rank": A.EP_HT_STAGE2_PER_RANK}[ht_stage2] \
         if isinstance(ht_stage2, str) else ht_stage2
+    c.ht_buffers = ht_buffers
     c.alloc_fn = alloc_fn if alloc_fn is not None else A.ALLOC_FN()
     c.free_fn = free_fn if free_fn is not None else A.FREE_FN()
     c.alloc_ctx = alloc_ctx

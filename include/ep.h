@@ -134,6 +134,10 @@ typedef struct {
     int32_t ll_buffers;          /* LL receive buffers used in turn: 1 or 2;
                                     0 means 2 (double buffering, NCCL-EP LL) */
     int32_t ht_stage2;           /* ep_ht_stage2_t (HT only)                   */
+    int32_t ht_buffers;          /* HT stage-row sets (stage-1 and stage-2 rows
+                                    with metadata) used in turn: 1 or 2; 0
+                                    means 1.  With 2 a dispatch may run while
+                                    the previous handle's rows are read.     */
     /* Optional allocator hooks: both or neither.  alloc_fn returns device
      * memory of at least `bytes` bytes aligned to 256, or NULL. */
     void *(*alloc_fn)(size_t bytes, void *ctx);
@@ -151,16 +155,17 @@ typedef struct ep_handle *ep_handle_t;
 /* Create a group (NCCL-EP ncclEpCreateGroup).  Validates the configuration
  * and allocates, once, every buffer the hot path writes, so that no call
  * below allocates device memory:
- *   LL: the fixed-slot receive space, expert-major, E x S x T_max messages
- *       of (row + 16) bytes; rank r's partition is experts
+ *   LL: ll_buffers fixed-slot receive spaces, expert-major, E x S x T_max
+ *       messages of (row + 16) bytes; rank r's partition is experts
  *       [r*E/R, (r+1)*E/R), i.e. a contiguous [E/R][S][T_max] block.
- *   HT: stage-1 rows (one per token and destination node) and stage-2 rows
- *       (one per token and expert), each with structure-of-arrays metadata,
- *       sized for the worst case S*T_max tokens.
+ *   HT: ht_buffers sets of stage-1 rows (one per token and destination
+ *       node) and stage-2 rows (one per token and expert), each with
+ *       structure-of-arrays metadata, sized for the worst case S*T_max tokens.
  *   Per handle slot: routing maps and counters for S*T_max tokens.
  * `stream` orders the initialisation.  On failure nothing stays allocated.
  * Errors: EP_ERR_INVALID_ARGUMENT (NULL pointers, inconsistent topology,
- * hidden not a multiple of 128 with FP8, only one allocator hook),
+ * hidden not a multiple of 128 with FP8, only one allocator hook,
+ * ll_buffers or ht_buffers outside 0..2),
  * EP_ERR_UNSUPPORTED (E > 1024, K > 32, N > 64, hidden > 16384,
  * num_src_ranks > R, or more LL slots, HT rows or map entries than 32-bit
  * indices address), EP_ERR_OUT_OF_MEMORY, EP_ERR_HIP. */
@@ -328,10 +333,11 @@ ep_status_t ep_layout_noalloc(const ep_config_t *config, const ep_tensor_t *topk
  * stage, and recv_counts must stay valid until then.  In LL the group keeps
  * ll_buffers receive buffers and each dispatch takes the next one in turn
  * (ep_handle_get_buffer returns the handle's); with two, a dispatch may be
- * in flight while the previous handle is combined.  In HT the group has one
- * set of stage-1 / stage-2 buffers: each HT dispatch overwrites the rows of
- * the group's previous one, so a handle's rows and partitions hold its data
- * until the next dispatch on the group (its maps and counts, and so its
+ * in flight while the previous handle is combined.  In HT the group keeps
+ * ht_buffers sets of stage-1 / stage-2 rows (1 unless configured) and each
+ * HT dispatch takes the next set in turn, overwriting the rows of the handle
+ * that used it before: a handle's rows and partitions hold its data until
+ * the dispatch that next takes its set (its maps and counts, and so its
  * combine, stay valid).
  *   tokens : BF16 [n, H] (n as in the handle), rows 16-byte aligned; or
  *            FP8_E4M3 [n, H] together with
@@ -413,13 +419,13 @@ typedef enum {
 } ep_buffer_t;
 ep_status_t ep_get_buffer(ep_group_t group, int32_t which, ep_tensor_t *view);
 
-/* As ep_get_buffer, but EP_BUF_LL_RECV is the receive buffer the handle's
- * last dispatch wrote (ep_get_buffer returns the first of the group's LL
- * buffers).  EP_ERR_INVALID_ARGUMENT for an LL handle not yet dispatched,
+/* As ep_get_buffer, but the receive buffer (LL) or stage-row set (HT) is
+ * the one the handle's last dispatch wrote (ep_get_buffer returns the
+ * group's first; an HT handle not yet dispatched gets the first set).  EP_ERR_INVALID_ARGUMENT for an LL handle not yet dispatched,
  * and for a handle whose rows a later dispatch on the group has overwritten:
- * in LL the next dispatch (of any handle) that takes the same receive
- * buffer -- the group's ll_buffers buffers are taken in turn --, in HT any
- * later dispatch.  The handle's maps, counts and combine stay valid. */
+ * the next dispatch (of any handle) that takes the same receive buffer or
+ * stage-row set -- the group's ll_buffers / ht_buffers of them are taken in
+ * turn.  The handle's maps, counts and combine stay valid. */
 ep_status_t ep_handle_get_buffer(ep_handle_t handle, int32_t which, ep_tensor_t *view);
 
 /* One destination rank's partition of a receive buffer: the view of

@@ -198,6 +198,27 @@ def test_ll_double_buffering_memory():
     assert sizes[2] - sizes[1] == one_buffer
 
 
+def test_ht_double_buffering_memory():
+    # one set of stage rows by default, two on request (the second dispatch of
+    # a two-micro-batch pipeline then leaves the first one's rows in place)
+    sizes = {}
+    for nbuf in (0, 1, 2):
+        pool = HostPool()
+        st, g = _create(_cfg(pool, max_tokens_per_rank=256, ht_buffers=nbuf))
+        assert st == A.EP_OK
+        b = ctypes.c_int64()
+        assert A.lib().ep_group_memory(g, ctypes.byref(b)) == A.EP_OK
+        sizes[nbuf] = b.value
+        A.lib().ep_destroy_group(g)
+        assert not pool.live
+    row_pitch = 7424
+    rows1, rows2 = 256 * 8, 256 * 8
+    assert sizes[0] == sizes[1]
+    assert sizes[2] - sizes[1] >= (rows1 + rows2) * row_pitch
+    for bad in (-1, 3):
+        assert _create(_cfg(HostPool(), ht_buffers=bad))[0] == A.EP_ERR_INVALID_ARGUMENT
+
+
 def test_per_rank_stage2_memory():
     # the per-rank stage 2 adds the received top-k ids and weights per row
     sizes = {}

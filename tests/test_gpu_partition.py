@@ -203,3 +203,65 @@ def test_ht_views_of_an_overwritten_handle_are_refused():
             ep.ep_destroy_handle(h)
     finally:
         ep.ep_destroy_group(g)
+
+
+def test_ht_double_buffered_stage_rows():
+    """With two HT stage-row sets, consecutive dispatches take them in turn:
+    two handles' rows stay in place side by side (each equal to the oracle's
+    rows for its own routing and tokens), a third dispatch takes the first
+    set again and only the first handle's views are refused; every handle's
+    combine stays valid."""
+    T, H = 300, 256
+    w = I.HT_PREFILL.with_(tokens_per_rank=T, hidden=H)
+    g = ep.ep_create_group(mode="ht", num_nodes=8, ranks_per_node=8, num_experts=256, top_k=8,
+                           max_nodes_per_token=4, hidden=H, max_tokens_per_rank=T, num_src_ranks=1,
+                           payload="fp8", max_handles=3, ht_buffers=2)
+    try:
+        hs, topks, xs = [], [], []
+        wts = I.normal_weights(T, 8, 70)
+        for j in range(3):
+            tk = torch.empty((T, 8), dtype=torch.int32, device="cuda")
+            hs.append(ep.ep_route_handle(g, dev(I.scores_for(w.with_(seed=70 + j))), tk))
+            topks.append(host(tk))
+            xs.append(I.normal_bf16(T, H, 71 + j))
+
+        def want(j):
+            lay = oracle.layout_ht(topks[j], 1, 256, 8, 8)
+            return lay, oracle.pack_ht(I.bf16_bits(xs[j]), topks[j], wts, T, 8, True, lay["node_row"],
+                                       lay["row2"], int(lay["c1"].sum()), int(lay["c2"].sum()))
+
+        def check(j):
+            lay, pk = want(j)
+            r1, r2 = int(lay["c1"].sum()), int(lay["c2"].sum())
+            np.testing.assert_array_equal(host(ep.ep_handle_get_buffer(hs[j], A.EP_BUF_HT_STAGE1)[:r1]), pk["stage1"])
+            np.testing.assert_array_equal(host(ep.ep_handle_get_buffer(hs[j], A.EP_BUF_HT_STAGE2)[:r2]), pk["stage2"])
+            np.testing.assert_array_equal(host(ep.ep_handle_get_buffer(hs[j], A.EP_BUF_HT_STAGE1_TOPK)[:r1]),
+                                          pk["meta1_topk"])
+            d = 11
+            p1 = host(ep.ep_get_partition(hs[j], d, A.EP_BUF_HT_STAGE1))
+            np.testing.assert_array_equal(p1, pk["stage1"][lay["off1"][d]:lay["off1"][d] + lay["c1"][d]])
+
+        ep.ep_dispatch(hs[0], xs[0].cuda(), topk_weights=dev(wts))
+        ep.ep_dispatch(hs[1], xs[1].cuda(), topk_weights=dev(wts))
+        check(0)
+        check(1)
+        assert ep.ep_handle_get_buffer(hs[0], A.EP_BUF_HT_STAGE2).data_ptr() != \
+            ep.ep_handle_get_buffer(hs[1], A.EP_BUF_HT_STAGE2).data_ptr()
+        ep.ep_dispatch(hs[2], xs[2].cuda(), topk_weights=dev(wts))
+        with pytest.raises(ep.EpError):
+            ep.ep_handle_get_buffer(hs[0], A.EP_BUF_HT_STAGE2)
+        with pytest.raises(ep.EpError):
+            ep.ep_get_partition(hs[0], 3, A.EP_BUF_HT_STAGE1)
+        check(1)
+        check(2)
+        for j in range(3):
+            lay, _ = want(j)
+            Y = I.normal_bf16(T * 8, H, 80 + j)
+            out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+            ep.ep_combine(hs[j], Y.cuda(), dev(wts), out)
+            np.testing.assert_array_equal(host(out), oracle.combine(I.bf16_bits(Y), wts, lay["row2"]))
+        assert ep.ep_get_device_error(g) == 0
+        for h in hs:
+            ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
