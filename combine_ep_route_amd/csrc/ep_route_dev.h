@@ -12,9 +12,11 @@
 // LPN = P/V lanes (a power of two).  All cross-lane steps are DPP row
 // permutations or ds_swizzle inside the 32-lane half, so nothing waits on LDS
 // except the single exchange of the N node scores.  The K experts come from a
-// merge tree (each lane sorts its V selection keys, five pairwise merges over
-// the exchange pattern leave the V best in every lane) when K <= V and V is a
-// power of two, else from K rounds of a 32-lane maximum.
+// tournament: each lane sorts its V selection keys (V a power of two), then K
+// rounds each take the 32-lane maximum of the lanes' heads and the lane that
+// held it moves its next key up.  (A merge tree -- five pairwise merges of
+// the lanes' sorted lists -- costs about 500 VALU operations per wave against
+// about 330 here.)  For other V, K rounds of a maximum over unsorted keys.
 #pragma once
 
 #include "ep_internal.h"
@@ -94,33 +96,6 @@ __device__ __forceinline__ void bitonic_sort_desc(uint64_t (&k)[V]) {
       }
 }
 
-// One level of the merge tree: the union of the lane's sorted V keys and its
-// partner's (exchange STEP) cut to its V largest, sorted.  max(mine[i],
-// partner[V-1-i]) is a bitonic sequence holding the V largest; a half-cleaner
-// cascade sorts it.  Both partners end with the same list.
-template <int STEP, int V>
-__device__ __forceinline__ void merge_level(uint64_t (&k)[V]) {
-  uint64_t o[V];
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint32_t hi = static_cast<uint32_t>(xchg<STEP>(static_cast<int>(k[i] >> 32)));
-    const uint32_t lo = static_cast<uint32_t>(xchg<STEP>(static_cast<int>(k[i])));
-    o[i] = (static_cast<uint64_t>(hi) << 32) | lo;
-  }
-#pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const uint64_t p = o[V - 1 - i];
-    k[i] = p > k[i] ? p : k[i];
-  }
-#pragma unroll
-  for (int stride = V >> 1; stride > 0; stride >>= 1)
-#pragma unroll
-    for (int i = 0; i < V; ++i) {
-      const int j = i ^ stride;
-      if (j > i) cx(k[i], k[j]);
-    }
-}
-
 // One exchange of a 32-lane maximum of 64-bit keys held as (hi, lo).
 template <int STEP>
 __device__ __forceinline__ void max_step(uint32_t& hi, uint32_t& lo) {
@@ -195,18 +170,25 @@ __device__ __forceinline__ int route_token_fast(const float* row, bool active, i
 #pragma unroll
   for (int v = 0; v < V; ++v) key[v] = keep ? select_key(val[v], e0 + v) : 0ull;
   int mine = -1;
-  if ((V & (V - 1)) == 0 && K <= V) {
-    // Merge tree: sort the lane's keys, then five levels of pairwise merges
-    // over the 32 lanes leave every lane with the token's V best, in order.
+  if ((V & (V - 1)) == 0) {
+    // Tournament: each lane sorts its V keys, then K rounds take the 32-lane
+    // maximum of the lanes' heads; the lane holding it (keys are distinct)
+    // moves its next key up.
     bitonic_sort_desc<V>(key);
-    merge_level<0, V>(key);
-    merge_level<1, V>(key);
-    merge_level<2, V>(key);
-    merge_level<3, V>(key);
-    merge_level<4, V>(key);
+    for (int k = 0; k < K; ++k) {
+      uint32_t hi = static_cast<uint32_t>(key[0] >> 32), lo = static_cast<uint32_t>(key[0]);
+      max_step<0>(hi, lo);
+      max_step<1>(hi, lo);
+      max_step<2>(hi, lo);
+      max_step<3>(hi, lo);
+      max_step<4>(hi, lo);
+      if (hl == k) mine = static_cast<int>(0xFFFFFFFFu - lo);
+      if (key[0] == ((static_cast<uint64_t>(hi) << 32) | lo)) {
 #pragma unroll
-    for (int v = 0; v < V; ++v)
-      if (hl == v) mine = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(key[v]));
+        for (int v = 0; v + 1 < V; ++v) key[v] = key[v + 1];
+        key[V - 1] = 0;
+      }
+    }
   } else {
     // K rounds of a 32-lane maximum of the lanes' best remaining keys.
     for (int k = 0; k < K; ++k) {
