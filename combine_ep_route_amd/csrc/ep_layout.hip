@@ -69,16 +69,35 @@ __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(LayoutArgs a) 
   const int E2 = a.E2, N = a.N, K = a.K, E = a.E;
   const int64_t i0 = static_cast<int64_t>(s) * a.T + t0;
   for (int x = tid; x < E2 + N; x += blockDim.x) s_mask[x] = 0;
+  // e / L and e / P by shifts when they are powers of two
+  auto div_l = [&](int e) { return a.l_shift >= 0 ? e >> a.l_shift : e / a.L; };
+  auto div_p = [&](int e) { return a.p_shift >= 0 ? e >> a.p_shift : e / a.P; };
+  // Routed entries are valid and distinct by construction: with one stage-2
+  // key per entry (the expert), the lanes that hold them set the mask bits
+  // directly (repeated node bits are harmless: the masks are ORs).
+  bool direct = false;
   if constexpr (ROUTE) {
     const int slot = tid >> 5, hl = tid & 31;
     const bool active = slot < ntok;
     const int64_t i = i0 + slot;
     const int mine = route_token_fast<V, LPN>(a.scores + (active ? i : 0) * a.ld, active, hl, s_node[slot], N,
                                               a.M, a.J, K);
-    if (hl < K) s_e[slot][hl] = mine;
-    if (active && hl < K) {
+    const bool held = active && hl < K;
+    if (held) {
       a.topk_out[i * K + hl] = mine;
       a.topk_copy[i * K + hl] = mine;
+    }
+    direct = !a.s2_rank;
+    if (direct) {
+      __syncthreads();   // the masks are zero
+      if (held) {
+        atomicOr(&s_mask[mine], 1u << slot);
+        if (a.ht) atomicOr(&s_mask[E2 + div_p(mine)], 1u << slot);
+      }
+      __syncthreads();
+      if (held) a.rank_e[i * K + hl] = __popc(s_mask[mine] & ((1u << slot) - 1u));
+    } else if (hl < K) {
+      s_e[slot][hl] = mine;
     }
   } else {
     for (int x = tid; x < ntok * K; x += blockDim.x) {
@@ -88,43 +107,42 @@ __global__ __launch_bounds__(kTileThreads) void tile_count_kernel(LayoutArgs a) 
       s_e[slot][k] = e;
     }
   }
-  __syncthreads();
-  // e / L and e / P by shifts when they are powers of two
-  auto div_l = [&](int e) { return a.l_shift >= 0 ? e >> a.l_shift : e / a.L; };
-  auto div_p = [&](int e) { return a.p_shift >= 0 ? e >> a.p_shift : e / a.P; };
-  // Entries: valid (in range, not a repeat), the stage-2 key (the expert, or
-  // with the per-rank stage 2 its rank, carried only by the token's first
-  // entry on it), and the first entry on each destination node.
-  int bad = 0;
-  for (int x = tid; x < ntok * K; x += blockDim.x) {
-    const int slot = x / K, k = x - slot * K;
-    const int e = s_e[slot][k];
-    const bool in_range = e >= 0 && e < E;
-    const int key = a.s2_rank ? div_l(e) : e;
-    const int nd = div_p(e);
-    bool dup = false, same_key = false, same_node = false;
-    for (int q = 0; q < k; ++q) {
-      const int eq = s_e[slot][q];
-      const bool inq = eq >= 0 && eq < E;
-      dup |= eq == e;
-      same_key |= inq && (a.s2_rank ? div_l(eq) : eq) == key;
-      same_node |= inq && div_p(eq) == nd;
+  if (!direct) {
+    __syncthreads();
+    // Entries: valid (in range, not a repeat), the stage-2 key (the expert,
+    // or with the per-rank stage 2 its rank, carried only by the token's
+    // first entry on it), and the first entry on each destination node.
+    int bad = 0;
+    for (int x = tid; x < ntok * K; x += blockDim.x) {
+      const int slot = x / K, k = x - slot * K;
+      const int e = s_e[slot][k];
+      const bool in_range = e >= 0 && e < E;
+      const int key = a.s2_rank ? div_l(e) : e;
+      const int nd = div_p(e);
+      bool dup = false, same_key = false, same_node = false;
+      for (int q = 0; q < k; ++q) {
+        const int eq = s_e[slot][q];
+        const bool inq = eq >= 0 && eq < E;
+        dup |= eq == e;
+        same_key |= inq && (a.s2_rank ? div_l(eq) : eq) == key;
+        same_node |= inq && div_p(eq) == nd;
+      }
+      const bool ok = in_range && !dup;
+      if (!in_range) bad |= EP_DEVERR_BAD_INDEX;
+      else if (dup) bad |= EP_DEVERR_DUP_INDEX;
+      const bool first = ok && !same_key;
+      if (first) atomicOr(&s_mask[key], 1u << slot);
+      if (a.ht && ok && !same_node) atomicOr(&s_mask[E2 + nd], 1u << slot);
+      s_key[slot][k] = first ? key : -1;
     }
-    const bool ok = in_range && !dup;
-    if (!in_range) bad |= EP_DEVERR_BAD_INDEX;
-    else if (dup) bad |= EP_DEVERR_DUP_INDEX;
-    const bool first = ok && !same_key;
-    if (first) atomicOr(&s_mask[key], 1u << slot);
-    if (a.ht && ok && !same_node) atomicOr(&s_mask[E2 + nd], 1u << slot);
-    s_key[slot][k] = first ? key : -1;
-  }
-  if (bad) atomicOr(a.err, bad);
-  __syncthreads();
-  // In-tile ranks: popcount of the key's mask below the token's lane.
-  for (int x = tid; x < ntok * K; x += blockDim.x) {
-    const int slot = x / K, k = x - slot * K;
-    const int key = s_key[slot][k];
-    a.rank_e[i0 * K + x] = key >= 0 ? __popc(s_mask[key] & ((1u << slot) - 1u)) : -1;
+    if (bad) atomicOr(a.err, bad);
+    __syncthreads();
+    // In-tile ranks: popcount of the key's mask below the token's lane.
+    for (int x = tid; x < ntok * K; x += blockDim.x) {
+      const int slot = x / K, k = x - slot * K;
+      const int key = s_key[slot][k];
+      a.rank_e[i0 * K + x] = key >= 0 ? __popc(s_mask[key] & ((1u << slot) - 1u)) : -1;
+    }
   }
   if (a.ht) {
     for (int x = tid; x < ntok * N; x += blockDim.x) {
