@@ -13,7 +13,8 @@
 // Mapping: a token is split over W waves, each owning a contiguous range of
 // 64*NV chunks (16 elements; 8 with a BF16 payload; lane l: chunks
 // c0 + v*64, v < NV); the waves of a workgroup (4 in HT, 2 in LL) work on
-// their own with no barriers -- each wave ranks its token itself.
+// their own -- each wave ranks its token itself.  The one exception is the
+// HT key offsets, which the workgroup scans into LDS once, at the start.
 //  1. The token's payload loads are issued first (16-byte loads).
 //  2. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 (IEEE fp32 division)
@@ -23,7 +24,8 @@
 //     for every finite bf16 amax).  Quantising comes before
 //     the positions, so the raw chunks' registers are free early.
 //  3. The token's rank inside its tile (from the handle) plus the tile's
-//     prefix (plus, in HT, the key's first row) gives every slot / row.
+//     prefix (plus, in HT, the key's first row from LDS) gives every
+//     slot / row.
 //     Positions are wave-uniform.
 //  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
 //     size rounded up to 128 B).  Each chunk of codes goes to every
@@ -191,6 +193,85 @@ __device__ __forceinline__ void put_scales(const DispatchArgs& p, const Raw (&ra
   }
 }
 
+// Waves per workgroup (every wave works on its own): 4 for HT and 2 for LL
+// were the fastest of 1, 2, 4 and 8 on the 4096-token prefill and the
+// 64 x 128-token decode dispatch.
+constexpr int kHtWavesPerGroup = 4;
+constexpr int kLlWavesPerGroup = 2;
+
+// HT key offsets.  The first stage-2 row of each key and the first stage-1
+// row of each rank are the exclusive prefix sums of the handle's per-key
+// totals (c2 [E2], c1 [R]).  Every workgroup scans them into LDS itself --
+// a few hundred values from L2 -- rather than wait for one workgroup of
+// the count pass to publish them.  A thread holds a contiguous run of each
+// array (kOffRun values at most); the runs' sums are scanned over the wave,
+// then across the waves through LDS.
+constexpr int kOffThreads = 64 * kHtWavesPerGroup;
+constexpr int kOffRun = ((kMaxExperts > kMaxRanks ? kMaxExperts : kMaxRanks) + kOffThreads - 1) / kOffThreads;
+
+struct KeyTotals {
+  int e[kOffRun], r[kOffRun];
+};
+
+__device__ __forceinline__ void load_totals(const DispatchArgs& p, int R, KeyTotals& t) {
+  const int tid = threadIdx.x;
+  const int pe = (p.E2 + kOffThreads - 1) / kOffThreads, pr = (R + kOffThreads - 1) / kOffThreads;
+#pragma unroll
+  for (int q = 0; q < kOffRun; ++q) {
+    t.e[q] = (q < pe && tid * pe + q < p.E2) ? p.c2[tid * pe + q] : 0;
+    t.r[q] = (q < pr && tid * pr + q < R) ? p.c1[tid * pr + q] : 0;
+  }
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  return v;
+}
+
+// s_off[0, E2): stage-2 key offsets; s_off[E2, E2 + R): stage-1 rank
+// offsets.  Workgroup 0 also writes them to the handle (off2, off1).  Every
+// thread of the workgroup takes part (two barriers).
+__device__ __forceinline__ void build_offsets(const DispatchArgs& p, int R, const KeyTotals& t, int32_t* s_off,
+                                              int* s_wave) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int E2 = p.E2;
+  const int pe = (E2 + kOffThreads - 1) / kOffThreads, pr = (R + kOffThreads - 1) / kOffThreads;
+  int se = 0, sr = 0;
+#pragma unroll
+  for (int q = 0; q < kOffRun; ++q) {
+    se += t.e[q];
+    sr += t.r[q];
+  }
+  const int ie = wave_inclusive_scan(se, lane), ir = wave_inclusive_scan(sr, lane);
+  if (lane == 63) {
+    s_wave[w] = ie;
+    s_wave[kHtWavesPerGroup + w] = ir;
+  }
+  __syncthreads();
+  int re = ie - se, rr = ir - sr;
+  for (int q = 0; q < w; ++q) {
+    re += s_wave[q];
+    rr += s_wave[kHtWavesPerGroup + q];
+  }
+#pragma unroll
+  for (int q = 0; q < kOffRun; ++q) {
+    if (q < pe && tid * pe + q < E2) s_off[tid * pe + q] = re;
+    re += t.e[q];
+    if (q < pr && tid * pr + q < R) s_off[E2 + tid * pr + q] = rr;
+    rr += t.r[q];
+  }
+  __syncthreads();
+  if (blockIdx.x == 0)
+    for (int x = tid; x < E2 + R; x += kOffThreads) {
+      if (x < E2) p.off2[x] = s_off[x];
+      else p.off1[x - E2] = s_off[x];
+    }
+}
+
 // Validity of the K entries of one token row: in range and not a repeat.
 template <int KMAX>
 __device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool present, int (&e)[KMAX],
@@ -208,10 +289,12 @@ __device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool p
 
 // A token spans W waves, blockDim.x / 64 waves per workgroup; a lane owns
 // chunks c = v*64 + lane, v < NV, of its wave's range (16 elements each; 8
-// with a BF16 payload, a plain 16-byte copy).  No barriers: everything shared
-// inside a token is wave-uniform.
+// with a BF16 payload, a plain 16-byte copy).  Past the HT key-offset scan
+// there are no barriers: everything shared inside a token is wave-uniform.
 template <int IN, bool HT, bool PAYLOAD, int KMAX, int NV>
 __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
+  extern __shared__ int32_t s_off[];   // HT: key offsets, [E2] stage-2 keys then [R] stage-1 ranks
+  __shared__ int s_wave[2 * kHtWavesPerGroup];
   const int lane = threadIdx.x & 63;
   const int C = IN == 1 ? p.H / 8 : p.H / 16;   // 16-byte chunks of the payload row
   const int K = p.K, E = p.E, N = p.N;
@@ -221,16 +304,29 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
   const int wpb = blockDim.x >> 6;                 // waves per workgroup
   const int64_t waves = static_cast<int64_t>(gridDim.x) * wpb;
   const int64_t total = p.n * W;
-  for (int64_t gw = static_cast<int64_t>(blockIdx.x) * wpb + (threadIdx.x >> 6); gw < total; gw += waves) {
+  const int64_t gw0 = static_cast<int64_t>(blockIdx.x) * wpb + (threadIdx.x >> 6);
+  // 1. Payload loads first, so they are in flight during the ranking.  The
+  //    first token's go out before the workgroup scans the HT key offsets,
+  //    whose own loads go out before them (loads complete in order, so the
+  //    scan waits for those alone).
+  Raw raw[NV];
+  auto load_token = [&](int64_t gw) {
+    const int64_t i = gw / W;
+    const int c0 = static_cast<int>(gw - i * W) * NV * 64 + lane;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) raw[v] = load_chunk<IN>(p, i, c0 + v * 64, c0 + v * 64 < C);
+  };
+  KeyTotals kt;
+  if constexpr (HT) load_totals(p, N * p.G, kt);
+  if constexpr (PAYLOAD)
+    if (gw0 < total) load_token(gw0);
+  if constexpr (HT) build_offsets(p, N * p.G, kt, s_off, s_wave);
+  for (int64_t gw = gw0; gw < total; gw += waves) {
     const int64_t i = gw / W;                       // token
     const int part = static_cast<int>(gw - i * W);  // which chunk range of it
     const int c0 = part * NV * 64 + lane;           // this lane's first chunk
-    // 1. Payload loads first, so they are in flight during the ranking.
-    Raw raw[NV];
-    if constexpr (PAYLOAD) {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) raw[v] = load_chunk<IN>(p, i, c0 + v * 64, c0 + v * 64 < C);
-    }
+    if constexpr (PAYLOAD)
+      if (gw != gw0) load_token(gw);
     const int s = static_cast<int>(i / p.T);
     const int t = static_cast<int>(i - static_cast<int64_t>(s) * p.T);
     const int j = s * p.tps + t / kTile;   // tile of this token
@@ -262,14 +358,14 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
         if (re >= 0) {
           const int key = (HT && p.s2_rank) ? me[k] / p.L : me[k];
           const int pre = p.hist_e[static_cast<int64_t>(j) * p.E2 + key] + re;
-          pos[k] = HT ? p.off2[key] + pre : (me[k] * p.S + s) * p.slots + pre;
+          pos[k] = HT ? s_off[key] + pre : (me[k] * p.S + s) * p.slots + pre;
         }
       }
     }
     // Stage-1 row of destination node n (uniform), or -1.
     auto node_pos = [&](int n) -> int {
       if (!((my_nodes >> n) & 1)) return -1;
-      return p.off1[n * p.G + s % p.G] + p.hist_n[static_cast<int64_t>(j) * N + n] + p.rank_n[i * N + n];
+      return s_off[p.E2 + n * p.G + s % p.G] + p.hist_n[static_cast<int64_t>(j) * N + n] + p.rank_n[i * N + n];
     };
 
     // 3. The handle's maps (written by the token's first wave).
@@ -438,12 +534,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(QuantArgs a, int W) {
 // full occupancy; a token spans W = ceil(C / (64*NV)) waves.
 constexpr int kChunksPerLane = 4;
 
-// Waves per workgroup (every wave works on its own): 4 for HT and 2 for LL
-// were the fastest of 1, 2, 4 and 8 on the 4096-token prefill and the
-// 64 x 128-token decode dispatch.
-constexpr int kHtWavesPerGroup = 4;
-constexpr int kLlWavesPerGroup = 2;
-
 template <int IN, bool PAYLOAD, int KMAX, int NV>
 void launch_nv(const DispatchArgs& p, hipStream_t stream) {
   const int C = IN == 1 ? p.H / 8 : p.H / 16;
@@ -455,7 +545,8 @@ void launch_nv(const DispatchArgs& p, hipStream_t stream) {
   if (cap > 0 && blocks > cap) blocks = cap;
   if (blocks > 0x7FFFFFFF) blocks = 0x7FFFFFFF;
   const dim3 grid(static_cast<unsigned>(blocks)), block(64 * wpb);
-  if (p.ht) dispatch_kernel<IN, true, PAYLOAD, KMAX, NV><<<grid, block, 0, stream>>>(p, W);
+  const size_t lds = static_cast<size_t>(p.E2 + p.N * p.G) * sizeof(int32_t);   // HT key offsets
+  if (p.ht) dispatch_kernel<IN, true, PAYLOAD, KMAX, NV><<<grid, block, lds, stream>>>(p, W);
   else dispatch_kernel<IN, false, PAYLOAD, KMAX, NV><<<grid, block, 0, stream>>>(p, W);
 }
 

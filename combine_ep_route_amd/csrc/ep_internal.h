@@ -103,7 +103,6 @@ struct Group {
   int buf_next = 0;                          // the one the next dispatch takes
   uint64_t buf_gen[2] = {0, 0};              // dispatches into each of them
   int32_t* err = nullptr;    // device error word
-  int32_t* done = nullptr;   // HT prefix scan: its workgroups finished (0 between launches)
 
   std::vector<Handle*> handles;
 
@@ -193,12 +192,9 @@ struct LayoutArgs {
   int32_t* ll_count;
   int32_t* node_row;
   int32_t* row2;
-  int32_t* c1;
-  int32_t* off1;
-  int32_t* c2;
-  int32_t* off2;
+  int32_t* c1;           // HT out: stage-1 rows per rank [R]
+  int32_t* c2;           // HT out: stage-2 rows per key [E2]
   int32_t* err;
-  int32_t* done;         // HT scan: workgroups finished (zero between launches)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 
@@ -232,8 +228,10 @@ struct DispatchArgs {
   const int32_t* rank_n;  // in-tile node ranks [n, N]
   const int32_t* hist_e;  // tile prefixes [tiles, E]
   const int32_t* hist_n;  // [tiles, N]
-  const int32_t* off1;    // HT: first stage-1 row of each rank [R]
-  const int32_t* off2;    // HT: first stage-2 row of each key [E2]
+  const int32_t* c1;      // HT: stage-1 rows per rank [R]
+  const int32_t* c2;      // HT: stage-2 rows per key [E2]
+  int32_t* off1;          // HT out: first stage-1 row of each rank [R] (their exclusive prefix sums)
+  int32_t* off2;          // HT out: first stage-2 row of each key [E2]
   int32_t* slot_map;      // LL out [n, K]
   int32_t* row2;          // HT out [n, K]
   int32_t* node_row;      // HT out [n, N]

@@ -19,11 +19,12 @@
 //     mask below the token's lane) and the tile's count per key;
 //   * scan_keys_kernel (HT): one wave per key turns the key's sequence of
 //     tile counts into exclusive prefix sums in place and writes the key's
-//     total; the workgroup that finishes last (a counter in the group,
-//     reset by that workgroup) scans the totals into the per-key offsets.
-//     LL: layout_scan_ll_kernel, one thread per (expert, source), since LL
-//     slots restart at 0 for every source;
-//   * the dispatch kernel adds key offset + tile prefix + in-tile rank.
+//     total.  LL: layout_scan_ll_kernel, one thread per (expert, source),
+//     since LL slots restart at 0 for every source;
+//   * the dispatch kernel adds key offset + tile prefix + in-tile rank; in
+//     HT each of its workgroups first scans the key totals into the key
+//     offsets in LDS (a few hundred values, read while its tokens load), so
+//     that no step of the scan waits for the other workgroups.
 // No atomics decide a position, so every map is bit-reproducible.
 #include "ep_route_dev.h"
 
@@ -183,41 +184,6 @@ __device__ __forceinline__ int wave_inclusive_scan(int v, int lane) {
 constexpr int kScanPerLane = 8;     // tile counts a lane holds per pass of a key's sequence
 constexpr int kScanThreads = 256;   // four keys per workgroup
 
-constexpr int kOffsetsPerThread = (kMaxExperts + kScanThreads - 1) / kScanThreads;
-
-// Exclusive prefix sums of c2[0, E2) into off2 and of c1[0, R) into off1 by
-// one workgroup of kScanThreads threads, both at once: each thread loads a
-// contiguous run of each (device-scope loads: other workgroups wrote them),
-// the runs' sums are scanned across the workgroup (wave shuffles, one LDS
-// exchange), then each thread writes its runs' prefixes.
-__device__ void key_offsets(const int32_t* c2, int32_t* off2, int E2, const int32_t* c1, int32_t* off1, int R,
-                            int* s_wave) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int pe = (E2 + kScanThreads - 1) / kScanThreads, pr = (R + kScanThreads - 1) / kScanThreads;
-  const int be = tid * pe, br = tid * pr;
-  int ve[kOffsetsPerThread], vr[kOffsetsPerThread];
-#pragma unroll
-  for (int q = 0; q < kOffsetsPerThread; ++q) {
-    ve[q] = (q < pe && be + q < E2) ? __hip_atomic_load(c2 + be + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-    vr[q] = (q < pr && br + q < R) ? __hip_atomic_load(c1 + br + q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
-  }
-  int se = 0, sr = 0;
-#pragma unroll
-  for (int q = 0; q < kOffsetsPerThread; ++q) { se += ve[q]; sr += vr[q]; }
-  const int ie = wave_inclusive_scan(se, lane), ir = wave_inclusive_scan(sr, lane);
-  if (lane == 63) { s_wave[w] = ie; s_wave[kScanThreads / 64 + w] = ir; }
-  __syncthreads();
-  int re = ie - se, rr = ir - sr;
-  for (int q = 0; q < w; ++q) { re += s_wave[q]; rr += s_wave[kScanThreads / 64 + q]; }
-#pragma unroll
-  for (int q = 0; q < kOffsetsPerThread; ++q) {
-    if (q < pe && be + q < E2) off2[be + q] = re;
-    re += ve[q];
-    if (q < pr && br + q < R) off1[br + q] = rr;
-    rr += vr[q];
-  }
-}
-
 // HT: one wave per key.  Keys [0, E2) are the stage-2 keys, whose sequence
 // is every tile in order; keys E2 + d (d = n*G + g, d < R) are the stage-1
 // ranks, whose sequence is the tiles of the sources s = g, g+G, g+2G, ...
@@ -226,8 +192,6 @@ __device__ void key_offsets(const int32_t* c2, int32_t* off2, int E2, const int3
 // scanned across the wave, and the exclusive prefixes are written back in
 // place; the key's total goes to c2 / c1.
 __global__ __launch_bounds__(kScanThreads) void scan_keys_kernel(LayoutArgs a) {
-  __shared__ int s_wave[2 * (kScanThreads / 64)];
-  __shared__ int s_last;
   const int lane = threadIdx.x & 63;
   const int key = blockIdx.x * (kScanThreads / 64) + (threadIdx.x >> 6);
   const int E2 = a.E2, N = a.N, G = a.G, R = N * G, tps = a.tps;
@@ -261,25 +225,8 @@ __global__ __launch_bounds__(kScanThreads) void scan_keys_kernel(LayoutArgs a) {
       }
       carry += __shfl(incl, 63, 64);
     }
-    // The total goes out as a device-scope store (written through to the
-    // device's coherence point), read by another workgroup below.
-    if (lane == 0)
-      __hip_atomic_store(expert ? a.c2 + key : a.c1 + d, carry, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (lane == 0) (expert ? a.c2 + key : a.c1 + d)[0] = carry;
   }
-  // The last workgroup to finish scans the key totals into the offsets.  Each
-  // wave waits for its stores to complete before the barrier, so the totals
-  // are in place before the workgroup's count is added; the last workgroup
-  // reads them after it has seen every other count.  (A device-scope release
-  // fence here would write back the whole L2 once per workgroup.)
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  if (threadIdx.x == 0)
-    s_last = __hip_atomic_fetch_add(a.done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-             static_cast<int>(gridDim.x) - 1;
-  __syncthreads();
-  if (!s_last) return;
-  key_offsets(a.c2, a.off2, E2, a.c1, a.off1, R, s_wave);
-  if (threadIdx.x == 0) __hip_atomic_store(a.done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Receive stage of a dispatch: the per-(expert, source) counters [E, S] as

@@ -5,8 +5,7 @@
 //
 // It runs the kernels of ep_create_handle (count tiles, prefix scan) and the
 // maps-only pass of the dispatch.  Their working storage -- the copy of
-// topk_idx, the in-tile ranks, the tile counts, the scan's finish counter
-// and the error word -- lives in `scratch`, a fixed device array of this
+// topk_idx, the in-tile ranks, the tile counts and the error word -- lives in `scratch`, a fixed device array of this
 // file, one copy per GPU, for the life of the process.  Host code never
 // passes the array's name to a kernel: once per device, with that device
 // current, hipGetSymbolAddress gives the device address, kept per device,
@@ -102,7 +101,7 @@ EP_API ep_status_t ep_layout_noalloc(const ep_config_t* config, const ep_tensor_
                        device_error->sizes[0] != 1 || !device_error->data))
     return EP_ERR_INVALID_ARGUMENT;
 
-  // Scratch: topk copy, in-tile ranks, tile counts, counter + error word.
+  // Scratch: topk copy, in-tile ranks, tile counts, error word.
   const int tps = static_cast<int>((T + kLayoutTile - 1) / kLayoutTile);
   const int64_t tiles = static_cast<int64_t>(tps) * S;
   const size_t need = align_up(n * K * 4) * 2 + (ht ? align_up(n * N * 4) : 0) +
@@ -125,14 +124,12 @@ EP_API ep_status_t ep_layout_noalloc(const ep_config_t* config, const ep_tensor_
   int32_t* rank_n = ht ? take(n * N * 4) : nullptr;
   int32_t* hist_e = take(static_cast<size_t>(tiles) * topo.E2 * 4);
   int32_t* hist_n = ht ? take(static_cast<size_t>(tiles) * N * 4) : nullptr;
-  int32_t* words = take(2 * 4);   // [0] error word, [1] the scan's finish counter
-  int32_t* err = device_error ? static_cast<int32_t*>(device_error->data) : words;
+  int32_t* err = device_error ? static_cast<int32_t*>(device_error->data) : take(4);
 
   auto out = [&](int m) { return static_cast<int32_t*>(maps[m]->data); };
-  // The counter and the error word start at zero (a fill kernel: no memset
-  // node, so the call can be captured).
-  hipError_t e = launch_fill_i32(words, 2, 0, s);
-  if (e == hipSuccess && device_error) e = launch_fill_i32(err, 1, 0, s);
+  // The error word starts at zero (a fill kernel: no memset node, so the
+  // call can be captured).
+  hipError_t e = launch_fill_i32(err, 1, 0, s);
   if (e != hipSuccess) return EP_ERR_HIP;
   if (n == 0) {
     // Nothing routed: zero counts and offsets.
@@ -175,14 +172,11 @@ EP_API ep_status_t ep_layout_noalloc(const ep_config_t* config, const ep_tensor_
   a.rank_n = rank_n;
   if (ht) {
     a.c1 = out(EP_MAP_HT_RANK_COUNT);
-    a.off1 = out(EP_MAP_HT_RANK_OFFSET);
     a.c2 = out(EP_MAP_HT_EXPERT_COUNT);
-    a.off2 = out(EP_MAP_HT_EXPERT_OFFSET);
   } else {
     a.ll_count = out(EP_MAP_LL_COUNT);
   }
   a.err = err;
-  a.done = words + 1;
   if ((e = launch_layout(a, s)) != hipSuccess) return EP_ERR_HIP;
 
   // The slot / row maps: the dispatch's maps-only pass.
@@ -209,8 +203,10 @@ EP_API ep_status_t ep_layout_noalloc(const ep_config_t* config, const ep_tensor_
   p.hist_e = hist_e;
   p.hist_n = hist_n;
   if (ht) {
-    p.off1 = a.off1;
-    p.off2 = a.off2;
+    p.c1 = a.c1;
+    p.c2 = a.c2;
+    p.off1 = out(EP_MAP_HT_RANK_OFFSET);
+    p.off2 = out(EP_MAP_HT_EXPERT_OFFSET);
     p.row2 = out(EP_MAP_HT_ROW);
     p.node_row = out(EP_MAP_HT_NODE_ROW);
   } else {

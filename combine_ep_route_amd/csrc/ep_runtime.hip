@@ -140,7 +140,7 @@ ep_status_t ensure_device(Group* g, hipStream_t stream) {
   if (g->dev_ready) return EP_OK;
   EP_HIP(hipGetDevice(&g->device));
   EP_HIP(hipDeviceGetAttribute(&g->num_cu, hipDeviceAttributeMultiprocessorCount, g->device));
-  EP_HIP(launch_fill_i32(g->err, 2, 0, stream));   // the error word and the scan counter
+  EP_HIP(launch_fill_i32(g->err, 1, 0, stream));   // the error word
   g->dev_ready = true;
   return EP_OK;
 }
@@ -199,6 +199,8 @@ DispatchArgs dispatch_base(const Handle* h) {
   p.rank_n = h->rank_n;
   p.hist_e = h->hist_e;
   p.hist_n = h->hist_n;
+  p.c1 = h->c1;
+  p.c2 = h->c2;
   p.off1 = h->off1;
   p.off2 = h->off2;
   p.slot_map = h->slot_map;
@@ -228,8 +230,8 @@ bool expert_rows(const Group* g, const ep_tensor_t* t, ep_tensor_t* out) {
   return check2d(out, EP_DTYPE_BF16, -1, g->cfg.hidden, EP_TAG_TOKENS, true);
 }
 
-// Make sure the slot / row maps exist (dispatch writes them; without a
-// dispatch, a maps-only pass computes them).
+// Make sure the slot / row maps and the HT key offsets exist (dispatch
+// writes them; without a dispatch, a maps-only pass computes them).
 ep_status_t ensure_maps(Handle* h, hipStream_t stream) {
   if (h->maps_ready) return EP_OK;
   DispatchArgs p = dispatch_base(h);
@@ -399,8 +401,7 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
     }
   }
   if (st == EP_OK) {
-    g->err = static_cast<int32_t*>(dev_alloc(g, 2 * sizeof(int32_t), &st));
-    g->done = g->err ? g->err + 1 : nullptr;
+    g->err = static_cast<int32_t*>(dev_alloc(g, sizeof(int32_t), &st));
   }
   for (int hs = 0; st == EP_OK && hs < cfg.max_handles; ++hs) {
     const size_t nm = static_cast<size_t>(g->n_max);
@@ -587,11 +588,8 @@ ep_status_t make_handle(Group* g, const int32_t* topk, const float* scores, int6
   a.node_row = h->node_row;
   a.row2 = h->row2;
   a.c1 = h->c1;
-  a.off1 = h->off1;
   a.c2 = h->c2;
-  a.off2 = h->off2;
   a.err = g->err;
-  a.done = g->done;
   h->maps_ready = (n == 0);
   h->buf_half = -1;
   h->dispatched = false;
@@ -686,7 +684,8 @@ EP_API ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tenso
   Group* g = h->g;
   const bool ll = g->cfg.mode == EP_MODE_LL;
   const int E = g->cfg.num_experts, K = g->cfg.top_k, N = g->cfg.num_nodes, S = g->cfg.num_src_ranks;
-  if (which == EP_MAP_LL_SLOT || which == EP_MAP_HT_NODE_ROW || which == EP_MAP_HT_ROW) {
+  if (which == EP_MAP_LL_SLOT || which == EP_MAP_HT_NODE_ROW || which == EP_MAP_HT_ROW ||
+      which == EP_MAP_HT_RANK_OFFSET || which == EP_MAP_HT_EXPERT_OFFSET) {
     if (const ep_status_t st = ensure_maps(h, h->stream); st != EP_OK) return st;
   }
   switch (which) {
@@ -904,6 +903,7 @@ EP_API ep_status_t ep_get_partition(ep_handle_t handle, int32_t rank, int32_t wh
     const bool stage1 = which >= EP_BUF_HT_STAGE1 && which <= EP_BUF_HT_STAGE1_WEIGHTS;
     const int keys = stage1 || g->s2_rank ? 1 : g->L;   // stage 2 per expert: the rank's L experts
     const int k0 = stage1 || g->s2_rank ? rank : rank * g->L;
+    if (const ep_status_t st = ensure_maps(h, h->stream); st != EP_OK) return st;   // writes the offsets
     const int32_t* off = nullptr;
     if (const ep_status_t st = read_counts(h, (stage1 ? h->off1 : h->off2) + k0, 1, &off); st != EP_OK) return st;
     first = *off;
