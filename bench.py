@@ -660,6 +660,9 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy three times (the reference "
                          "kernel for scaling HBM byte counters), then exit")
+    ap.add_argument("--calibrate-fill", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device fill of BYTES bytes three times (a write-only "
+                         "reference kernel for the dispatch's write rate), then exit")
     args = ap.parse_args(argv)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: the 64 EP ranks are partitions of one MI355X's HBM; "
@@ -677,6 +680,14 @@ def main(argv=None):
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "device copy", "bytes_read_per_launch": 1 << 30,
                           "bytes_written_per_launch": 1 << 30, "launches": 3}), flush=True)
+        return 0
+    if args.calibrate_fill > 0:
+        dst = torch.empty(args.calibrate_fill // 4, dtype=torch.int32, device="cuda")
+        for _ in range(3):
+            dst.fill_(1)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device fill", "bytes_written_per_launch": dst.numel() * 4,
+                          "launches": 3}), flush=True)
         return 0
 
     import combine_ep_route_amd as ep

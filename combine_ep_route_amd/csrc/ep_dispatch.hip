@@ -272,182 +272,202 @@ __device__ __forceinline__ void build_offsets(const DispatchArgs& p, int R, cons
     }
 }
 
-// Validity of the K entries of one token row: in range and not a repeat.
-template <int KMAX>
-__device__ __forceinline__ void entries(const int32_t* row, int K, int E, bool present, int (&e)[KMAX],
-                                        bool (&ok)[KMAX]) {
+// The inputs of one token's positions, all loaded in one round trip before
+// its payload: lane k < K holds entry k (expert id, in-tile rank, weight),
+// lane n < N node n (in-tile rank and tile prefix), and when the tile's
+// prefix row has at most kRowKeys keys every lane holds four consecutive
+// ones, so that no load waits for the token's expert ids.
+constexpr int kRowKeys = 256;
+
+struct PosIn {
+  int e, re, rn, hn;
+  float w;
+  int h[4];
+};
+
+template <bool HT, bool META>
+__device__ __forceinline__ void load_pos(const DispatchArgs& p, int i, int j, int lane, bool meta, PosIn& q) {
+  const int K = p.K;
+  const bool lk = lane < K;
+  q.e = lk ? p.topk[static_cast<int64_t>(i) * K + lane] : -1;
+  q.re = lk ? p.rank_e[static_cast<int64_t>(i) * K + lane] : -1;
+  q.w = (HT && META && meta && lk && p.w) ? p.w[static_cast<int64_t>(i) * K + lane] : 0.0f;
+  if (p.E2 <= kRowKeys) {
+    const int32_t* row = p.hist_e + static_cast<int64_t>(j) * p.E2;
 #pragma unroll
-  for (int k = 0; k < KMAX; ++k) e[k] = (present && k < K) ? row[k] : -1;
-#pragma unroll
-  for (int k = 0; k < KMAX; ++k) {
-    bool dup = false;
-#pragma unroll
-    for (int j = 0; j < k; ++j) dup |= e[j] == e[k];
-    ok[k] = present && k < K && e[k] >= 0 && e[k] < E && !dup;
+    for (int c = 0; c < 4; ++c) q.h[c] = 4 * lane + c < p.E2 ? row[4 * lane + c] : 0;
   }
+  if constexpr (HT) {
+    const bool ln = lane < p.N;
+    q.rn = ln ? p.rank_n[static_cast<int64_t>(i) * p.N + lane] : -1;
+    q.hn = ln ? p.hist_n[static_cast<int64_t>(j) * p.N + lane] : 0;
+  }
+}
+
+// Token gw / W's coordinates; the wave index is uniform, so these are scalar.
+struct TokenAt {
+  int i, part, s, t, j;
+};
+__device__ __forceinline__ TokenAt token_at(const DispatchArgs& p, uint32_t gw, uint32_t W) {
+  TokenAt a;
+  a.i = static_cast<int>(gw / W);
+  a.part = static_cast<int>(gw - static_cast<uint32_t>(a.i) * W);
+  a.s = static_cast<int>(static_cast<uint32_t>(a.i) / static_cast<uint32_t>(p.T));
+  a.t = a.i - a.s * p.T;
+  a.j = a.s * p.tps + a.t / kTile;
+  return a;
 }
 
 // A token spans W waves, blockDim.x / 64 waves per workgroup; a lane owns
 // chunks c = v*64 + lane, v < NV, of its wave's range (16 elements each; 8
 // with a BF16 payload, a plain 16-byte copy).  Past the HT key-offset scan
 // there are no barriers: everything shared inside a token is wave-uniform.
+// The token's entries are worked on lane by lane (lane k: entry k, lane n:
+// node n), and each row's position is read out of its lane when the row is
+// written.
 template <int IN, bool HT, bool PAYLOAD, int KMAX, int NV>
-__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
+__global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W_) {
   extern __shared__ int32_t s_off[];   // HT: key offsets, [E2] stage-2 keys then [R] stage-1 ranks
   __shared__ int s_wave[2 * kHtWavesPerGroup];
   const int lane = threadIdx.x & 63;
   const int C = IN == 1 ? p.H / 8 : p.H / 16;   // 16-byte chunks of the payload row
   const int K = p.K, E = p.E, N = p.N;
+  const uint32_t W = static_cast<uint32_t>(W_);
   // Rows end on whole 128-byte lines when the scale bytes (H/32) are whole
   // 16-byte groups, so the LL header is 16-byte aligned: H % 512 == 0.
   const bool line_tail = (p.H & 511) == 0;
-  const int wpb = blockDim.x >> 6;                 // waves per workgroup
-  const int64_t waves = static_cast<int64_t>(gridDim.x) * wpb;
-  const int64_t total = p.n * W;
-  const int64_t gw0 = static_cast<int64_t>(blockIdx.x) * wpb + (threadIdx.x >> 6);
-  // 1. Payload loads first, so they are in flight during the ranking.  The
-  //    first token's go out before the workgroup scans the HT key offsets,
-  //    whose own loads go out before them (loads complete in order, so the
-  //    scan waits for those alone).
+  const uint32_t wpb = blockDim.x >> 6;            // waves per workgroup
+  const uint32_t waves = gridDim.x * wpb;
+  const uint32_t total = static_cast<uint32_t>(p.n) * W;
+  const uint32_t gw0 = blockIdx.x * wpb + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool row_keys = p.E2 <= kRowKeys;
+  // 1. Loads, in the order their results are needed (loads complete in
+  //    order): the HT key totals, the first token's position inputs, then
+  //    its payload; the workgroup scans the key offsets while the payload
+  //    is in flight.
   Raw raw[NV];
-  auto load_token = [&](int64_t gw) {
-    const int64_t i = gw / W;
-    const int c0 = static_cast<int>(gw - i * W) * NV * 64 + lane;
+  auto load_token = [&](const TokenAt& a) {
+    const int c0 = a.part * NV * 64 + lane;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) raw[v] = load_chunk<IN>(p, i, c0 + v * 64, c0 + v * 64 < C);
+    for (int v = 0; v < NV; ++v) raw[v] = load_chunk<IN>(p, a.i, c0 + v * 64, c0 + v * 64 < C);
   };
   KeyTotals kt;
   if constexpr (HT) load_totals(p, N * p.G, kt);
-  if constexpr (PAYLOAD)
-    if (gw0 < total) load_token(gw0);
+  PosIn q;
+  if (gw0 < total) {
+    const TokenAt a = token_at(p, gw0, W);
+    load_pos<HT, PAYLOAD>(p, a.i, a.j, lane, a.part == 0, q);
+    if constexpr (PAYLOAD) load_token(a);
+  }
   if constexpr (HT) build_offsets(p, N * p.G, kt, s_off, s_wave);
-  for (int64_t gw = gw0; gw < total; gw += waves) {
-    const int64_t i = gw / W;                       // token
-    const int part = static_cast<int>(gw - i * W);  // which chunk range of it
+  for (uint32_t gw = gw0; gw < total; gw += waves) {
+    const TokenAt a = token_at(p, gw, W);
+    const int i = a.i, part = a.part, s = a.s, t = a.t, j = a.j;
     const int c0 = part * NV * 64 + lane;           // this lane's first chunk
-    if constexpr (PAYLOAD)
-      if (gw != gw0) load_token(gw);
-    const int s = static_cast<int>(i / p.T);
-    const int t = static_cast<int>(i - static_cast<int64_t>(s) * p.T);
-    const int j = s * p.tps + t / kTile;   // tile of this token
+    if (gw != gw0) {
+      load_pos<HT, PAYLOAD>(p, i, j, lane, part == 0, q);
+      if constexpr (PAYLOAD) load_token(a);
+    }
+    const bool meta = part == 0;                    // the token's first wave writes maps and metadata
 
-    // 2. This token's entries (uniform) plus the handle's in-tile ranks and
-    //    tile prefixes give every slot / row (wave-uniform scalar loads).
-    int me[KMAX];
-    bool mok[KMAX];
-    entries<KMAX>(p.topk + i * K, K, E, true, me, mok);
+    // 2. Entries (lane k): valid when in range and not a repeat of an
+    //    earlier entry; the first valid entry on each node carries the
+    //    node's stage-1 row.  Uniform copies of the entries come from
+    //    their lanes.
+    const int e = q.e;
+    const int nd = e >= 0 ? e / p.P : -1;
+    bool dup = false;
+#pragma unroll
+    for (int k = 0; k < KMAX - 1; ++k) {
+      const int ek = __builtin_amdgcn_readlane(e, k);
+      dup |= k < lane && ek == e;
+    }
+    const bool ok = lane < K && e >= 0 && e < E && !dup;
+    const uint64_t okm = __ballot(ok);
     // Quantise as soon as the payload is in, so that the raw chunks'
-    // registers are free before the positions are worked out (3 us less per
-    // 4096 tokens than quantising after them).
+    // registers are free before the positions are worked out.
     if constexpr (PAYLOAD && IN == 0) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) quantize(raw[v]);
     }
-    uint64_t my_nodes = 0;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k)
-      if (mok[k]) my_nodes |= 1ull << (me[k] / p.P);
-    // An entry without a stage-2 row of its own (invalid, or with the
-    // per-rank stage 2 not the token's first entry on its rank) has rank -1.
-    int pos[KMAX];
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      pos[k] = -1;
-      if (mok[k] && k < K) {
-        const int re = p.rank_e[i * K + k];
-        if (re >= 0) {
-          const int key = (HT && p.s2_rank) ? me[k] / p.L : me[k];
-          const int pre = p.hist_e[static_cast<int64_t>(j) * p.E2 + key] + re;
-          pos[k] = HT ? s_off[key] + pre : (me[k] * p.S + s) * p.slots + pre;
-        }
-      }
-    }
-    // Stage-1 row of destination node n (uniform), or -1.
-    auto node_pos = [&](int n) -> int {
-      if (!((my_nodes >> n) & 1)) return -1;
-      return s_off[p.E2 + n * p.G + s % p.G] + p.hist_n[static_cast<int64_t>(j) * N + n] + p.rank_n[i * N + n];
-    };
 
-    // 3. The handle's maps (written by the token's first wave).
-    if (part == 0 && lane < K) {
-      int v = -1;
+    // 3. Positions.  Stage 2 / LL (lane k): key offset + tile prefix +
+    //    in-tile rank; an entry without a row of its own (invalid, or with
+    //    the per-rank stage 2 not the token's first entry on its rank) has
+    //    in-tile rank -1.  Stage 1 (lane n): the node's rank offset + tile
+    //    prefix + in-tile rank, or -1 when the token does not go there.
+    const bool has2 = ok && q.re >= 0;
+    const int key = (HT && p.s2_rank) ? (e >= 0 ? e / p.L : 0) : e;
+    int pre;
+    if (row_keys) {
+      // the tile prefix of `key` sits in lane key/4, element key%4
+      const int src = has2 ? key >> 2 : 0;
+      int hv = 0;
 #pragma unroll
-      for (int k = 0; k < KMAX; ++k)
-        if (k == lane) v = pos[k];
-      (HT ? p.row2 : p.slot_map)[i * K + lane] = v;
-    }
-    if (HT && part == 0) {
-      for (int n = 0; n < N; ++n) {
-        const int r = node_pos(n);
-        if (lane == (n & 63)) p.node_row[i * N + n] = r;
+      for (int c = 0; c < 4; ++c) {
+        const int v = __shfl(q.h[c], src, 64);
+        if ((key & 3) == c) hv = v;
       }
+      pre = hv;
+    } else {
+      pre = has2 ? p.hist_e[static_cast<int64_t>(j) * p.E2 + key] : 0;
     }
+    int pos = -1;
+    if (has2) pos = HT ? s_off[key] + pre + q.re : (e * p.S + s) * p.slots + pre + q.re;
+    int node_pos = -1, row1 = -1;
+    if constexpr (HT) {
+      if (lane < N && q.rn >= 0) node_pos = s_off[p.E2 + lane * p.G + s % p.G] + q.hn + q.rn;
+      bool same_node = false;
+#pragma unroll
+      for (int k = 0; k < KMAX - 1; ++k) {
+        const int nk = __builtin_amdgcn_readlane(nd, k);
+        same_node |= k < lane && ((okm >> k) & 1) && nk == nd;
+      }
+      const int r = __shfl(node_pos, (ok && !same_node) ? nd : 0, 64);
+      if (ok && !same_node) row1 = r;
+    }
+
+    // 4. The handle's maps.
+    if (meta && lane < K) (HT ? p.row2 : p.slot_map)[static_cast<int64_t>(i) * K + lane] = pos;
+    if (HT && meta && lane < N) p.node_row[static_cast<int64_t>(i) * N + lane] = node_pos;
 
     if constexpr (PAYLOAD) {
-      // 4. Stage-1 destinations as a per-entry list: entry k carries the row
-      //    of its node if it is the token's first entry on that node.
-      int row1[KMAX];
-#pragma unroll
-      for (int k = 0; k < KMAX; ++k) {
-        row1[k] = -1;
-        if (HT && mok[k]) {
-          const int nk = me[k] / p.P;
-          bool first = true;
-#pragma unroll
-          for (int q = 0; q < k; ++q) first &= !(mok[q] && me[q] / p.P == nk);
-          if (first) row1[k] = node_pos(nk);
-        }
-      }
       // 5. Metadata of every row (the token's first wave).
-      if (part != 0) {
+      if (!meta) {
       } else if constexpr (HT) {
-#pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-          const int32_t r = row1[k];
-          if (r < 0) continue;
-          if (lane == 0) {
-            p.m1_tok[r] = t;
-            p.m1_src[r] = s;
-          }
-          if (lane < K) {
-            int ev = -1;
-#pragma unroll
-            for (int q = 0; q < KMAX; ++q)
-              if (q == lane) ev = me[q];
-            p.m1_topk[static_cast<int64_t>(r) * K + lane] = ev;
-            if (p.w) p.m1_w[static_cast<int64_t>(r) * K + lane] = p.w[i * K + lane];
-          }
+        if (row1 >= 0) {
+          p.m1_tok[row1] = t;
+          p.m1_src[row1] = s;
         }
 #pragma unroll
         for (int k = 0; k < KMAX; ++k) {
-          const int32_t r = pos[k];
-          if (r >= 0 && lane == 0) {
-            p.m2_src[r] = s;
-            p.m2_tok[r] = t;
-            p.m2_k[r] = k;
-          }
-          if (p.s2_rank && r >= 0 && lane < K) {
-            // the token's entries on this row's rank, as local expert ids
-            const int rk = me[k] / p.L;
-            int ev = -1;
-            bool okv = false;
-#pragma unroll
-            for (int q = 0; q < KMAX; ++q)
-              if (q == lane) { ev = me[q]; okv = mok[q]; }
-            const bool here = okv && ev / p.L == rk;
-            p.m2_topk[static_cast<int64_t>(r) * K + lane] = here ? ev - rk * p.L : -1;
-            p.m2_w[static_cast<int64_t>(r) * K + lane] = (here && p.w) ? p.w[i * K + lane] : 0.0f;
+          const int r = __builtin_amdgcn_readlane(row1, k);
+          if (r >= 0 && lane < K) {
+            p.m1_topk[static_cast<int64_t>(r) * K + lane] = e;
+            if (p.w) p.m1_w[static_cast<int64_t>(r) * K + lane] = q.w;
           }
         }
-      } else if (!line_tail) {
+        if (pos >= 0) {
+          p.m2_src[pos] = s;
+          p.m2_tok[pos] = t;
+          p.m2_k[pos] = lane;
+        }
+        if (p.s2_rank) {
+          // the token's entries on each row's rank, as local expert ids
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k) {
-          const int32_t slot = pos[k];
-          if (slot >= 0 && lane == 0) {
-            const i32x4 hdr{t, s, k, 0};
-            __builtin_nontemporal_store(hdr, reinterpret_cast<i32x4*>(p.ll_buf + static_cast<int64_t>(slot) * p.msg_pitch + p.row_bytes));
+          for (int k = 0; k < KMAX; ++k) {
+            const int r = __builtin_amdgcn_readlane(pos, k);
+            if (r >= 0 && lane < K) {
+              const int rk = __builtin_amdgcn_readlane(key, k);
+              const bool here = ok && key == rk;
+              p.m2_topk[static_cast<int64_t>(r) * K + lane] = here ? e - rk * p.L : -1;
+              p.m2_w[static_cast<int64_t>(r) * K + lane] = (here && p.w) ? q.w : 0.0f;
+            }
           }
         }
+      } else if (!line_tail && pos >= 0) {
+        const i32x4 hdr{t, s, lane, 0};
+        __builtin_nontemporal_store(hdr, reinterpret_cast<i32x4*>(p.ll_buf + static_cast<int64_t>(pos) * p.msg_pitch + p.row_bytes));
       }
       // 6. Gather the scales, then write each destination row with NV code
       //    stores and one scale store.
@@ -458,7 +478,7 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
       // payload (BF16) to the next 128-byte boundary: the scales, the LL
       // header, then zeros, so that no cache line of a row is written in
       // part.  The last wave of the token writes it, 16 bytes per lane.
-      const bool tail_here = line_tail && part == W - 1;
+      const bool tail_here = line_tail && part == static_cast<int>(W) - 1;
       const int tail_off = IN == 1 ? 2 * p.H : p.H + 4 * b0;
       const int tail_sc = IN == 1 ? 0 : ((C >> 3) - b0) >> 2;   // 16-byte groups of scales
       const int tail_end = static_cast<int>(((HT ? p.row_bytes : p.row_bytes + 16) + 127) & ~int64_t{127});
@@ -479,15 +499,21 @@ __global__ __launch_bounds__(256) void dispatch_kernel(DispatchArgs p, int W) {
       };
       if constexpr (HT) {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-          if (row1[k] >= 0) put_row(p.st1 + static_cast<int64_t>(row1[k]) * p.row_pitch, k);
+        for (int k = 0; k < KMAX; ++k) {
+          const int r = __builtin_amdgcn_readlane(row1, k);
+          if (r >= 0) put_row(p.st1 + static_cast<int64_t>(r) * p.row_pitch, k);
+        }
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-          if (pos[k] >= 0) put_row(p.st2 + static_cast<int64_t>(pos[k]) * p.row_pitch, k);
+        for (int k = 0; k < KMAX; ++k) {
+          const int r = __builtin_amdgcn_readlane(pos, k);
+          if (r >= 0) put_row(p.st2 + static_cast<int64_t>(r) * p.row_pitch, k);
+        }
       } else {
 #pragma unroll
-        for (int k = 0; k < KMAX; ++k)
-          if (pos[k] >= 0) put_row(p.ll_buf + static_cast<int64_t>(pos[k]) * p.msg_pitch, k);
+        for (int k = 0; k < KMAX; ++k) {
+          const int r = __builtin_amdgcn_readlane(pos, k);
+          if (r >= 0) put_row(p.ll_buf + static_cast<int64_t>(r) * p.msg_pitch, k);
+        }
       }
     }
   }

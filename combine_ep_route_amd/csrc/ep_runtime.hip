@@ -349,9 +349,11 @@ EP_API ep_status_t ep_create_group(const ep_config_t* cfg_in, ep_stream_t stream
   g->rows1_max = g->n_max * nodes_per_token;
   g->rows2_max = g->n_max * K;
   const int64_t tps = (Tm + kLayoutTile - 1) / kLayoutTile;
-  // Slot, row and map indices are 32-bit on the device.
+  // Slot, row and map indices are 32-bit on the device, and so is the
+  // dispatch's wave count (a token spans up to ceil(H/8 / 256) waves).
   const int64_t kIndexMax = INT32_MAX;
-  if (g->n_max * std::max<int64_t>(K, N) > kIndexMax || g->rows2_max > kIndexMax ||
+  const int64_t waves_per_token = (cfg.hidden / 8 + 255) / 256;
+  if (g->n_max * std::max<int64_t>({K, N, waves_per_token}) > kIndexMax || g->rows2_max > kIndexMax ||
       (cfg.mode == EP_MODE_LL && static_cast<int64_t>(E) * S * Tm > kIndexMax) ||
       S * tps * std::max<int64_t>(E, N) > kIndexMax) {
     delete g;
