@@ -279,6 +279,10 @@ typedef enum {
                                     (PER_RANK: [R] rows per rank)             */
     EP_MAP_HT_EXPERT_OFFSET = 7  /* exclusive prefix sum of the above          */
 } ep_map_t;
+/* The counts are written when the handle is made.  The slot / row maps and
+ * the HT offsets are written by the handle's dispatch; asked for before a
+ * dispatch has run, they are computed by a maps-only pass that this call
+ * enqueues on the handle's stream (no rows are written). */
 ep_status_t ep_handle_get_map(ep_handle_t handle, int32_t which, ep_tensor_t *view);
 
 /* The handle's maps and counts without a group and without allocating:
