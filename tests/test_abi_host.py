@@ -133,6 +133,10 @@ def test_invalid_config_rejected_before_hip(bad):
     # more HT stage-2 rows (S * T_max * K) than 32-bit indices address
     dict(num_nodes=32, ranks_per_node=32, num_experts=1024, top_k=32, num_src_ranks=1024,
          max_tokens_per_rank=1 << 17),
+    # more dispatch waves (S * T_max tokens, up to 8 waves per token at hidden 16384) than
+    # 32-bit indices address, with every row and slot count still in range
+    dict(num_nodes=2, ranks_per_node=1, num_experts=4, top_k=2, max_nodes_per_token=2, hidden=16384,
+         num_src_ranks=64, max_tokens_per_rank=1 << 23),
 ])
 def test_unsupported_config(bad):
     pool = HostPool()
