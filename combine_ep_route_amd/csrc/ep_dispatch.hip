@@ -15,7 +15,11 @@
 // c0 + v*64, v < NV); the waves of a workgroup (4 in HT, 2 in LL) work on
 // their own -- each wave ranks its token itself.  The one exception is the
 // HT key offsets, which the workgroup scans into LDS once, at the start.
-//  1. The token's payload loads are issued first (16-byte loads).
+//  1. Loads, in the order their results are needed (they complete in
+//     order): the inputs of the token's positions -- its entries, their
+//     in-tile ranks, its node ranks and its tile's prefix row, lane by lane
+//     -- then the payload (16-byte loads).  Everything a position needs
+//     arrives in one round trip.
 //  2. A 128-element block is 8 consecutive lanes; its amax is a 3-step
 //     xor-shuffle inside a DPP row.  scale = amax/448 (IEEE fp32 division)
 //     and q = E4M3(x/scale), the quotient by a refined reciprocal and one
@@ -23,10 +27,10 @@
 //     scale is tiny (the tests compare the codes with the IEEE quotient's
 //     for every finite bf16 amax).  Quantising comes before
 //     the positions, so the raw chunks' registers are free early.
-//  3. The token's rank inside its tile (from the handle) plus the tile's
-//     prefix (plus, in HT, the key's first row from LDS) gives every
-//     slot / row.
-//     Positions are wave-uniform.
+//  3. Lane k works out entry k's slot / row: its rank inside its tile plus
+//     the tile's prefix (plus, in HT, the key's first row from LDS); lane n
+//     does node n's stage-1 row.  Each row's position is read out of its
+//     lane when the row is written.
 //  4. Rows start on 128-byte boundaries (the buffers' row pitch is the row
 //     size rounded up to 128 B).  Each chunk of codes goes to every
 //     destination row with non-temporal stores (nothing on this GPU reads
