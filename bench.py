@@ -123,8 +123,8 @@ MIN_CPU_SECONDS = 8.0   # each leg of the CPU baseline runs at least this long (
 
 def host_threads():
     """Host threads the multi-core oracle leg uses: the CPUs this process may
-    run on, capped by OMP_NUM_THREADS when it is set (the GPU machine sets it to
-    its CPU share)."""
+    run on, capped by OMP_NUM_THREADS when it is set (a shared host may set
+    it to this job's CPU share)."""
     avail = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
     cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
     return max(1, min(avail, cap) if cap > 0 else avail)
