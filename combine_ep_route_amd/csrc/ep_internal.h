@@ -182,19 +182,16 @@ struct LayoutArgs {
   int L;                 // experts per rank
   int s2_rank;           // HT stage 2 per (token, rank): key = e / L, first entry only
   int l_shift, p_shift;  // log2 of L and P when powers of two, else -1
-  int tps, n_tiles;
-  int32_t* hist_e;
-  int32_t* hist_n;
+  int tps, n_tiles;      // tiles per source, tiles in all
+  int32_t* hist_e;       // [tiles, E2] per-tile key counts, rewritten as prefixes over the key's tiles
+  int32_t* hist_n;       // [tiles, N] the same per destination node (HT)
   int32_t* topk_copy;    // [n, K]
   int32_t* rank_e;       // [n, K] out: in-tile ranks
   int32_t* rank_n;       // [n, N] out: in-tile node ranks (HT)
-  int32_t* slot_map;
-  int32_t* ll_count;
-  int32_t* node_row;
-  int32_t* row2;
+  int32_t* ll_count;     // LL out: slots used per (expert, source) [E, S]
   int32_t* c1;           // HT out: stage-1 rows per rank [R]
   int32_t* c2;           // HT out: stage-2 rows per key [E2]
-  int32_t* err;
+  int32_t* err;          // device error word (bad or repeated entries)
 };
 hipError_t launch_layout(const LayoutArgs& a, hipStream_t stream);
 

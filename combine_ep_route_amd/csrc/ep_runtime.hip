@@ -585,10 +585,7 @@ ep_status_t make_handle(Group* g, const int32_t* topk, const float* scores, int6
   a.topk_copy = h->topk;
   a.rank_e = h->rank_e;
   a.rank_n = h->rank_n;
-  a.slot_map = h->slot_map;
   a.ll_count = h->ll_count;
-  a.node_row = h->node_row;
-  a.row2 = h->row2;
   a.c1 = h->c1;
   a.c2 = h->c2;
   a.err = g->err;
