@@ -29,6 +29,38 @@ def _ht_group(S, T, E, N, G, K, H, stage2="expert"):
                               payload="fp8", ht_stage2=stage2)
 
 
+def test_ht_partition_bounds_before_any_dispatch():
+    """An HT handle that no dispatch has used yet: its partition views take
+    their bounds from the rank and expert offsets, which the maps-only pass
+    computes when the views are asked for (the rows hold data only once a
+    dispatch has run)."""
+    S, T, E, N, G, K, H = 2, 90, 64, 4, 2, 4, 256
+    R, L = N * G, E // (N * G)
+    say(f"HT partition bounds before a dispatch: S={S} T={T} E={E} R={R} K={K}")
+    topk = I.random_topk(S * T, E, K, seed=74)
+    g = _ht_group(S, T, E, N, G, K, H)
+    try:
+        h = ep.ep_create_handle(g, dev(topk))
+        lay = oracle.layout_ht(topk, S, E, N, G)
+        st1, st2 = buffer(g, A.EP_BUF_HT_STAGE1), buffer(g, A.EP_BUF_HT_STAGE2)
+        for r in range(R):
+            o, c = int(lay["off1"][r]), int(lay["c1"][r])
+            p1 = ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE1)
+            assert tuple(p1.shape) == (c, st1.shape[1])
+            if c:
+                assert p1.data_ptr() == st1[o].data_ptr()
+            o2, c2 = int(lay["off2"][r * L]), int(lay["c2"][r * L:(r + 1) * L].sum())
+            p2 = ep.ep_get_partition(h, r, A.EP_BUF_HT_STAGE2)
+            assert tuple(p2.shape) == (c2, st2.shape[1])
+            if c2:
+                assert p2.data_ptr() == st2[o2].data_ptr()
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_NODE_ROW), lay["node_row"])
+        np.testing.assert_array_equal(get_map(h, A.EP_MAP_HT_ROW), lay["row2"])
+        ep.ep_destroy_handle(h)
+    finally:
+        ep.ep_destroy_group(g)
+
+
 def test_ht_partitions_are_the_ranks_rows():
     S, T, E, N, G, K, H = 3, 200, 64, 4, 2, 4, 256
     R, L = N * G, E // (N * G)
