@@ -255,10 +255,12 @@ def ll_cpu_baseline(T=128):
                 seconds=round(dt, 3), sources=done, tokens_per_s=round(T * done / dt, 1))
 
 
-def time_steps(step, args, stream, out_of, ep, g, n_calls=3):
+def time_steps(step, args, stream, out_of, ep, g, n_calls=3, replays=None):
     """Warm-up, an eager pass with events around every call (per-call ms),
     then (graph mode) one captured step per input set, replayed; the graph's
-    output must equal the eager output of the same step."""
+    output must equal the eager output of the same step.  The first timed
+    replay gives ms_per_step; with `replays` (a list) three more replays are
+    timed the same way and appended to it, to show the run-to-run spread."""
     log(f"[bench] warmup {args.warmup}")
     for j in range(args.warmup):
         step(j)
@@ -298,6 +300,12 @@ def time_steps(step, args, stream, out_of, ep, g, n_calls=3):
         graph.replay()
         torch.cuda.synchronize()
         ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+        if replays is not None:
+            for _ in range(3):
+                t0 = time.perf_counter()
+                graph.replay()
+                torch.cuda.synchronize()
+                replays.append((time.perf_counter() - t0) * 1e3 / args.steps)
         assert ep.ep_get_device_error(g) == 0
         ref = out_of(0).clone()
         step(0)
@@ -337,7 +345,7 @@ STEP_CALLS = ["route_handle", "dispatch", "combine"]
 
 
 def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic_ok, pct,
-                traffic_file=TRAFFIC_FILE):
+                traffic_file=TRAFFIC_FILE, replays=None):
     names = STEP_CALLS
     ms = dict(zip(names, mean_ms))
     value = ab["total"] / (ms_per_step * 1e-3) / 1e9
@@ -354,6 +362,8 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
         "ms_per_step": round(ms_per_step, 5),
         "execution": args.mode,
         "ms_per_step_eager": round(ms_eager, 5),
+        # three more replays of the same graph after the timed one
+        "ms_per_step_replays": [round(r, 5) for r in (replays or [])],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -383,7 +393,8 @@ def result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config, traffic
 
 def secondary_line(r):
     """The compact form of another workload's result line."""
-    return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"], "gbs": r["value"],
+    return {"workload": r["config"]["workload"], "ms_per_step": r["ms_per_step"],
+            "ms_per_step_replays": r["ms_per_step_replays"], "gbs": r["value"],
             "frac_of_hbm_peak": r["frac_of_hbm_peak"], "tokens_per_s": r["tokens_per_s"],
             "algorithmic_bytes_per_step": r["config"]["algorithmic_bytes_per_step"],
             "kernel_ms": r["kernel_ms"], "roofline": r["roofline"]}
@@ -450,7 +461,9 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
     ep.ep_destroy_handle(h)
     ab = algorithmic_bytes(n_tok, K, H, rows1, rows2, E, per_rank)
 
-    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
+    replays = []
+    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g,
+                                                     replays=replays)
     if round_trip:
         name = f"ht_round_trip_{n_tok}_zipf"
     else:
@@ -463,7 +476,7 @@ def run_ht(args, ep, per_rank=False, node_limit=4, w=I.HT_PREFILL):
     traffic_file = (TRAFFIC_FILE_ROUND_TRIP if round_trip else TRAFFIC_FILE_PER_RANK if per_rank
                     else TRAFFIC_FILE_NO_LIMIT if node_limit == 0 else TRAFFIC_FILE)
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
-                         traffic_ok=True, pct=pct, traffic_file=traffic_file)
+                         traffic_ok=True, pct=pct, traffic_file=traffic_file, replays=replays)
     result["cpu_sync_us"] = time_cpu_sync(ep, g, sets[0])
     if per_rank:
         result["formats"] = "fp8_e4m3 payload / bf16 combine of per-rank partial rows, fp32 accumulate"
@@ -532,7 +545,9 @@ def run_ll(args, ep, S, payload="fp8"):
         ep.ep_destroy_handle(h)
 
     ab = ll_algorithmic_bytes(n_tok, K, H, E, S, fp8=payload == "fp8")
-    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g)
+    replays = []
+    mean_ms, ms_eager, ms_per_step, pct = time_steps(step, args, stream, lambda j: sets[j]["out"], ep, g,
+                                                     replays=replays)
     suffix = "" if payload == "fp8" else "_bf16"
     config = {"workload": f"ll_decode_{S}x{T}{suffix}_plus_combine", "tokens": n_tok, "sources": S,
               "tokens_per_source": T, "hidden": H, "experts": E, "top_k": K, "nodes": 8,
@@ -540,7 +555,8 @@ def run_ll(args, ep, S, payload="fp8"):
               "algorithmic_bytes_per_step": ab["total"]}
     result = result_line(args, ab, mean_ms, ms_eager, ms_per_step, n_tok, config,
                          traffic_ok=S == 64, pct=pct,
-                         traffic_file=TRAFFIC_FILE_LL if payload == "fp8" else TRAFFIC_FILE_LL_BF16)
+                         traffic_file=TRAFFIC_FILE_LL if payload == "fp8" else TRAFFIC_FILE_LL_BF16,
+                         replays=replays)
     if payload != "fp8":
         result["formats"] = "bf16 payload / bf16 combine, fp32 accumulate"
     result["us_per_call"] = {k: round(float(v) * 1e3, 2) for k, v in zip(STEP_CALLS, mean_ms)}

@@ -42,6 +42,9 @@ def test_bench_json_line():
     assert 0 < d["value"] < 8000.0 and 0 < rf["achieved"] < 8000.0
     assert "cpu_baseline" not in d and "secondary" not in d
     assert set(d["kernel_ms"]) == {"route_handle", "dispatch", "combine"}
+    # three more replays of the timed graph, each a plausible step time
+    reps = d["ms_per_step_replays"]
+    assert len(reps) == 3 and all(0.2 * d["ms_per_step"] < r < 5 * d["ms_per_step"] for r in reps)
 
 
 def test_bench_secondary_lines():
@@ -65,3 +68,4 @@ def test_bench_secondary_lines():
             <= 0.01 * line["gbs"]
         assert line["roofline"]["kernel"] in ("dispatch", "combine")
         assert 0 < line["gbs"] < 8000.0
+        assert len(line["ms_per_step_replays"]) == 3
